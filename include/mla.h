@@ -1,0 +1,185 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) library for Multi-head Latent
+ * Attention decode over a paged, prefix-shared latent KV cache.
+ *
+ * The operation (TokenSpeed code-audit article, complete technology list,
+ * MLA kernel entry): every token stores ONE row of d_latent latent values
+ * followed by d_rope rope values (512 + 64 in DeepSeek-style models); that row
+ * is the key of every query head, and its latent part is the value.  The
+ * per-head key and value up-projections are absorbed into the query (the
+ * query arrives as q_absorbed, d_latent wide, plus q_rope, d_rope wide) and
+ * into the caller's output projection, so for request b, query token t, head h
+ *
+ *   z_j   = scale * ( q_absorbed[b,t,h,:] . c_j  +  q_rope[b,t,h,:] . k_j )
+ *   o     = sum_j softmax(z)_j * c_j              (d_latent wide)
+ *   lse   = ln sum_j exp(z_j)
+ *
+ * over the visible tokens j of request b.  Rows live in fixed-size pages
+ * found through a per-request block table (the "推理优化" tag page,
+ * PagedAttention article: logical block -> physical block); several requests
+ * may point at the same physical pages for a shared prefix (TokenSpeed 580
+ * tok/s zero-copy article: prefix KV shared by reference, never copied).
+ *
+ * Long contexts run in two stages, as the code-audit article describes the
+ * Blackwell kernel: a split stage writes fp32 partial results per chunk of
+ * the sequence into a workspace, and a reduction stage merges them by
+ * log-sum-exp rescaling and casts to the output type.  mla_decode() runs both;
+ * mla_decode_split() and mla_combine() expose them separately.
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers unless marked "host"; the
+ *     caller owns every buffer.  The library allocates no device memory,
+ *     keeps no state between calls and never synchronises the stream (except
+ *     in checked mode, see MLA_CHECK below).
+ *   - Work is enqueued on `stream` in order; results are ready when the
+ *     stream reaches that point.  Calls on different streams may overlap.
+ *   - Every function returns an mla_status code; no C++ exception crosses
+ *     the ABI.  Arguments are validated on the host before any HIP call, so
+ *     a non-zero status means nothing was enqueued.  Device faults, if any,
+ *     surface at the caller's next synchronisation.
+ *   - Contents of page-table entries at or past ceil(seq_len/page_size) and of
+ *     page slots at or past seq_len are never used (they may hold anything,
+ *     including -1 and NaN).  In-range entries must be valid page ids: this
+ *     is a precondition (not clamped), checked only in checked mode.
+ *   - Checked mode: with the environment variable MLA_CHECK=1 at library
+ *     load time, mla_decode() and mla_decode_split() copy page_table and
+ *     seq_lens to the host (synchronising the stream) and return
+ *     MLA_ERR_CHECK if any used page id is outside [0, num_pages) or any
+ *     seq_len is outside [0, max_pages_per_seq * page_size].  Never use it
+ *     under graph capture.
+ */
+#ifndef MLA_DECODE_H_
+#define MLA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_DTYPE_F32 = 0,      /* IEEE binary32 */
+  MLA_DTYPE_BF16 = 1,     /* bfloat16 (upper half of binary32) */
+  MLA_DTYPE_FP8_E4M3 = 2  /* OCP FP8 E4M3: 4 exponent bits, 3 mantissa bits, max 448
+                             ("推理优化" tag page, quantisation article, FP8 table);
+                             KV only, with one fp32 scale per token */
+} mla_dtype;
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shape */
+  MLA_ERR_UNSUPPORTED = -2, /* well-formed, but no kernel for this combination */
+  MLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than mla_workspace_size() */
+  MLA_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  MLA_ERR_CHECK = -5        /* checked mode found a bad page id or seq_len */
+} mla_status;
+
+/* Shape and types of one decode call (host struct, passed by pointer). */
+typedef struct {
+  int32_t batch;             /* B >= 0: requests */
+  int32_t q_len;             /* T >= 1: query tokens per request (1 = plain decode;
+                                >1 = speculative drafts, folded with the heads into
+                                one row axis of T*H rows as the code-audit article's
+                                fold_sq_factor does) */
+  int32_t num_heads;         /* H >= 1 */
+  int32_t d_latent;          /* Dc >= 1: latent width, also the output width */
+  int32_t d_rope;            /* Dr >= 0: rope width */
+  int32_t page_size;         /* P >= 1: tokens per page */
+  int32_t num_pages;         /* NP >= 1: physical pages in kv_pages */
+  int32_t max_pages_per_seq; /* MP >= 1: columns of page_table */
+  int32_t max_seq_len;       /* host-known upper bound on seq_lens, used only to plan
+                                splits; 0 means MP * P */
+  int32_t q_dtype;           /* mla_dtype of q_absorbed and q_rope: F32 or BF16 */
+  int32_t kv_dtype;          /* mla_dtype of kv_pages: F32, BF16 or FP8_E4M3 */
+  int32_t out_dtype;         /* mla_dtype of out: F32 or BF16 */
+  int32_t causal;            /* 0: every query token sees j < L_b.  1: query token t
+                                sees j <= L_b - T + t (the T drafts are the last T
+                                stored rows and form a linear chain) */
+  int32_t num_splits;        /* 0: the library chooses; >= 1 forces S chunks */
+} mla_problem;
+
+/*
+ * Number of sequence chunks S that mla_decode() will use for this problem
+ * (>= 1), written to *num_splits.  Chunk k of request b covers tokens
+ * [k C_b, min((k+1) C_b, L_b)) with C_b = P * ceil(ceil(L_b / S) / P), so
+ * chunks are page aligned and empty chunks are allowed.
+ */
+int mla_num_splits(const mla_problem* problem, int32_t* num_splits);
+
+/* Bytes of device workspace mla_decode() needs (0 when S == 1), to *bytes. */
+int mla_workspace_size(const mla_problem* problem, size_t* bytes);
+
+/*
+ * Full decode: split stage plus (when S > 1) the merge, on `stream`.
+ *   q_absorbed [B, T, H, Dc]  q_dtype, row-major
+ *   q_rope     [B, T, H, Dr]  q_dtype (may be NULL when Dr == 0)
+ *   kv_pages   [NP, P, Dc+Dr] kv_dtype; row = Dc latent values then Dr rope values
+ *   kv_scales  [NP, P] fp32 per-token scale for FP8_E4M3 KV (stored value =
+ *              e4m3(code) * scale); must be NULL for other KV types
+ *   page_table [B, MP] int32 physical page ids
+ *   seq_lens   [B] int32, 0 <= L_b <= MP * P
+ *   scale      softmax scale applied to the full (Dc + Dr)-deep dot product
+ *   out        [B, T, H, Dc] out_dtype
+ *   lse        [B, T, H] fp32 natural-log log-sum-exp, or NULL
+ *   workspace  >= mla_workspace_size() bytes, 256-byte aligned (NULL if 0)
+ * Rows with no visible token get out = 0 and lse = -inf.
+ */
+int mla_decode(const mla_problem* problem, const void* q_absorbed, const void* q_rope,
+               const void* kv_pages, const float* kv_scales, const int32_t* page_table,
+               const int32_t* seq_lens, float scale, void* out, float* lse, void* workspace,
+               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Split stage only, with S = num_splits >= 1 chunks (problem->num_splits is
+ * ignored).  Writes, per request b, chunk k and row r = t * H + h:
+ *   partial_o   [B, S, T*H, Dc] fp32: that chunk's softmax-weighted latent sum,
+ *               already divided by the chunk's own normaliser
+ *   partial_lse [B, S, T*H] fp32: the chunk's natural-log log-sum-exp, -inf
+ *               (with partial_o = 0) when the chunk sees no token
+ */
+int mla_decode_split(const mla_problem* problem, const void* q_absorbed, const void* q_rope,
+                     const void* kv_pages, const float* kv_scales, const int32_t* page_table,
+                     const int32_t* seq_lens, float scale, int32_t num_splits,
+                     float* partial_o, float* partial_lse, hipStream_t stream);
+
+/*
+ * Merge stage: for each of batch*rows rows, M = max_k lse_k,
+ * w_k = exp(lse_k - M), out = sum_k w_k o_k / sum_k w_k cast to out_dtype,
+ * lse = M + ln sum_k w_k (written if lse != NULL); chunks with lse = -inf
+ * weigh nothing and a row with no live chunk gives out = 0, lse = -inf
+ * (code-audit article: reduction kernel doing log-sum-exp rescale-merge and
+ * the cast to BF16).  Layouts are those of mla_decode_split().
+ */
+int mla_combine(int32_t batch, int32_t num_splits, int32_t rows, int32_t d_latent,
+                const float* partial_o, const float* partial_lse, int32_t out_dtype,
+                void* out, float* lse, hipStream_t stream);
+
+/*
+ * Test hook for the page-table loader: copies, bit for bit, the stored rows
+ * of logical token tok[i] of request req[i] (i < n) into out [n, Dc+Dr]
+ * (kv_dtype elements), resolving pages with the same device address routine
+ * the decode kernels use.  req/tok are device arrays; entries must satisfy
+ * 0 <= req < B and 0 <= tok < MP * P with a valid page id (precondition).
+ */
+int mla_gather_rows(const mla_problem* problem, const void* kv_pages, const int32_t* page_table,
+                    int32_t n, const int32_t* req, const int32_t* tok, void* out,
+                    hipStream_t stream);
+
+/*
+ * Host-side table check (the one checked mode runs): page_table_host [B, MP]
+ * and seq_lens_host [B] are HOST arrays.  Returns MLA_OK, MLA_ERR_CHECK or
+ * MLA_ERR_INVALID_ARG.
+ */
+int mla_check_tables(const mla_problem* problem, const int32_t* page_table_host,
+                     const int32_t* seq_lens_host);
+
+/* Static description of a status code (never NULL). */
+const char* mla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H_ */

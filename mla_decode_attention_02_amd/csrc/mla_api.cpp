@@ -1,0 +1,269 @@
+// C-ABI layer of the MLA decode library: argument validation, split
+// planning, checked mode and kernel dispatch.  Declared in include/mla.h.
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <vector>
+
+#include "../../include/mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+using mla::SplitParams;
+
+// Largest chunk count the planner picks by itself, and the number of
+// workgroups it aims for (256 CUs, one 4-wave MFMA workgroup each, two waves
+// of workgroups so that short and long chunks even out).
+constexpr int32_t kAutoMaxSplits = 64;
+constexpr int64_t kTargetWorkgroups = 512;
+constexpr int32_t kMaxSplits = 1 << 16;
+
+bool env_checked_mode() {
+  static const bool on = [] {
+    const char* v = getenv("MLA_CHECK");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+// MLA_KERNEL=generic routes every call to the VALU kernel (cross-checks).
+bool env_force_generic() {
+  const char* v = getenv("MLA_KERNEL");
+  return v && v[0] == 'g';
+}
+
+bool valid_dtype(int32_t d) { return d == MLA_DTYPE_F32 || d == MLA_DTYPE_BF16 || d == MLA_DTYPE_FP8_E4M3; }
+
+int validate_problem(const mla_problem* pr) {
+  if (!pr) return MLA_ERR_INVALID_ARG;
+  if (pr->batch < 0 || pr->q_len < 1 || pr->num_heads < 1 || pr->d_latent < 1 || pr->d_rope < 0 ||
+      pr->page_size < 1 || pr->num_pages < 1 || pr->max_pages_per_seq < 1 || pr->max_seq_len < 0 ||
+      pr->num_splits < 0 || pr->num_splits > kMaxSplits)
+    return MLA_ERR_INVALID_ARG;
+  if ((int64_t)pr->max_pages_per_seq * pr->page_size > INT32_MAX) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)pr->max_seq_len > (int64_t)pr->max_pages_per_seq * pr->page_size) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)pr->q_len * pr->num_heads > INT32_MAX / 4) return MLA_ERR_INVALID_ARG;
+  if (pr->causal != 0 && pr->causal != 1) return MLA_ERR_INVALID_ARG;
+  if (!valid_dtype(pr->q_dtype) || !valid_dtype(pr->kv_dtype) || !valid_dtype(pr->out_dtype))
+    return MLA_ERR_INVALID_ARG;
+  if (pr->q_dtype == MLA_DTYPE_FP8_E4M3 || pr->out_dtype == MLA_DTYPE_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
+  if (pr->d_latent > 1024 || pr->d_latent + pr->d_rope > 4096) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+int32_t effective_max_len(const mla_problem* pr) {
+  return pr->max_seq_len > 0 ? pr->max_seq_len : pr->max_pages_per_seq * pr->page_size;
+}
+
+// Chunks per request: forced, or enough (page-aligned) chunks that the grid
+// reaches about kTargetWorkgroups workgroups, never more than the pages of
+// the longest request.
+int32_t plan_splits(const mla_problem* pr) {
+  const int32_t max_pages = (effective_max_len(pr) + pr->page_size - 1) / pr->page_size;
+  const int32_t cap = max_pages > 0 ? max_pages : 1;
+  if (pr->num_splits > 0) return pr->num_splits;
+  const int64_t rows = (int64_t)pr->q_len * pr->num_heads;
+  const int64_t groups = (rows + 127) / 128;
+  const int64_t units = (int64_t)(pr->batch > 0 ? pr->batch : 1) * groups;
+  int64_t s = (kTargetWorkgroups + units - 1) / units;
+  if (s > kAutoMaxSplits) s = kAutoMaxSplits;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
+size_t partial_bytes(const mla_problem* pr, int32_t S) {
+  const size_t rows = (size_t)pr->batch * S * pr->q_len * pr->num_heads;
+  const size_t o = rows * pr->d_latent * sizeof(float);
+  const size_t o_aligned = (o + 255) & ~(size_t)255;
+  return o_aligned + rows * sizeof(float);
+}
+
+SplitParams make_params(const mla_problem* pr, const void* q_abs, const void* q_rope, const void* kv,
+                        const float* kv_scales, const int32_t* page_table, const int32_t* seq_lens,
+                        float scale, int32_t S) {
+  SplitParams p{};
+  p.B = pr->batch;
+  p.T = pr->q_len;
+  p.H = pr->num_heads;
+  p.Dc = pr->d_latent;
+  p.Dr = pr->d_rope;
+  p.P = pr->page_size;
+  p.NP = pr->num_pages;
+  p.MP = pr->max_pages_per_seq;
+  p.q_dtype = pr->q_dtype;
+  p.kv_dtype = pr->kv_dtype;
+  p.out_dtype = pr->out_dtype;
+  p.causal = pr->causal;
+  p.S = S;
+  p.q_abs = q_abs;
+  p.q_rope = q_rope;
+  p.kv = kv;
+  p.kv_scales = kv_scales;
+  p.page_table = page_table;
+  p.seq_lens = seq_lens;
+  p.scale = scale;
+  p.force_generic = env_force_generic();
+  return p;
+}
+
+int validate_inputs(const mla_problem* pr, const void* q_abs, const void* q_rope, const void* kv,
+                    const float* kv_scales, const int32_t* page_table, const int32_t* seq_lens) {
+  if (pr->batch == 0) return MLA_OK;
+  if (!q_abs || !kv || !page_table || !seq_lens) return MLA_ERR_INVALID_ARG;
+  if (pr->d_rope > 0 && !q_rope) return MLA_ERR_INVALID_ARG;
+  if ((pr->kv_dtype == MLA_DTYPE_FP8_E4M3) != (kv_scales != nullptr)) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+int run_checked_mode(const mla_problem* pr, const int32_t* page_table, const int32_t* seq_lens,
+                     hipStream_t stream) {
+  if (!env_checked_mode() || pr->batch == 0) return MLA_OK;
+  std::vector<int32_t> pt((size_t)pr->batch * pr->max_pages_per_seq), sl((size_t)pr->batch);
+  if (hipMemcpyAsync(pt.data(), page_table, pt.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipMemcpyAsync(sl.data(), seq_lens, sl.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  return mla_check_tables(pr, pt.data(), sl.data());
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_num_splits(const mla_problem* problem, int32_t* num_splits) {
+  const int rc = validate_problem(problem);
+  if (rc) return rc;
+  if (!num_splits) return MLA_ERR_INVALID_ARG;
+  *num_splits = plan_splits(problem);
+  return MLA_OK;
+}
+
+int mla_workspace_size(const mla_problem* problem, size_t* bytes) {
+  const int rc = validate_problem(problem);
+  if (rc) return rc;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  const int32_t S = plan_splits(problem);
+  *bytes = S > 1 ? partial_bytes(problem, S) : 0;
+  return MLA_OK;
+}
+
+int mla_check_tables(const mla_problem* problem, const int32_t* page_table_host,
+                     const int32_t* seq_lens_host) {
+  const int rc = validate_problem(problem);
+  if (rc) return rc;
+  if (problem->batch > 0 && (!page_table_host || !seq_lens_host)) return MLA_ERR_INVALID_ARG;
+  const int64_t cap = (int64_t)problem->max_pages_per_seq * problem->page_size;
+  for (int32_t b = 0; b < problem->batch; ++b) {
+    const int32_t L = seq_lens_host[b];
+    if (L < 0 || L > cap) return MLA_ERR_CHECK;
+    const int32_t used = (int32_t)(((int64_t)L + problem->page_size - 1) / problem->page_size);
+    for (int32_t e = 0; e < used; ++e) {
+      const int32_t page = page_table_host[(int64_t)b * problem->max_pages_per_seq + e];
+      if (page < 0 || page >= problem->num_pages) return MLA_ERR_CHECK;
+    }
+  }
+  return MLA_OK;
+}
+
+int mla_decode_split(const mla_problem* problem, const void* q_absorbed, const void* q_rope,
+                     const void* kv_pages, const float* kv_scales, const int32_t* page_table,
+                     const int32_t* seq_lens, float scale, int32_t num_splits, float* partial_o,
+                     float* partial_lse, hipStream_t stream) {
+  int rc = validate_problem(problem);
+  if (rc) return rc;
+  if (num_splits < 1 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
+  rc = validate_inputs(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table, seq_lens);
+  if (rc) return rc;
+  if (problem->batch == 0) return MLA_OK;
+  if (!partial_o || !partial_lse) return MLA_ERR_INVALID_ARG;
+  rc = run_checked_mode(problem, page_table, seq_lens, stream);
+  if (rc) return rc;
+  SplitParams p = make_params(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table,
+                              seq_lens, scale, num_splits);
+  p.write_final = false;
+  p.part_o = partial_o;
+  p.part_lse = partial_lse;
+  return mla::launch_split(p, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_decode(const mla_problem* problem, const void* q_absorbed, const void* q_rope,
+               const void* kv_pages, const float* kv_scales, const int32_t* page_table,
+               const int32_t* seq_lens, float scale, void* out, float* lse, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  int rc = validate_problem(problem);
+  if (rc) return rc;
+  rc = validate_inputs(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table, seq_lens);
+  if (rc) return rc;
+  if (problem->batch == 0) return MLA_OK;
+  if (!out) return MLA_ERR_INVALID_ARG;
+  const int32_t S = plan_splits(problem);
+  const size_t need = S > 1 ? partial_bytes(problem, S) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
+    return MLA_ERR_WORKSPACE;
+  rc = run_checked_mode(problem, page_table, seq_lens, stream);
+  if (rc) return rc;
+  SplitParams p = make_params(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table,
+                              seq_lens, scale, S);
+  if (S == 1) {
+    p.write_final = true;
+    p.out = out;
+    p.lse = lse;
+    return mla::launch_split(p, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
+  const int32_t rows = problem->q_len * problem->num_heads;
+  const size_t o_bytes = (size_t)problem->batch * S * rows * problem->d_latent * sizeof(float);
+  p.write_final = false;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)((char*)workspace + ((o_bytes + 255) & ~(size_t)255));
+  if (mla::launch_split(p, stream) != hipSuccess) return MLA_ERR_HIP;
+  return mla::launch_combine(problem->batch, S, rows, problem->d_latent, p.part_o, p.part_lse,
+                             problem->out_dtype, out, lse, stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+int mla_combine(int32_t batch, int32_t num_splits, int32_t rows, int32_t d_latent,
+                const float* partial_o, const float* partial_lse, int32_t out_dtype, void* out,
+                float* lse, hipStream_t stream) {
+  if (batch < 0 || num_splits < 1 || num_splits > kMaxSplits || rows < 1 || d_latent < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (out_dtype != MLA_DTYPE_F32 && out_dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!partial_o || !partial_lse || !out) return MLA_ERR_INVALID_ARG;
+  return mla::launch_combine(batch, num_splits, rows, d_latent, partial_o, partial_lse, out_dtype,
+                             out, lse, stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+int mla_gather_rows(const mla_problem* problem, const void* kv_pages, const int32_t* page_table,
+                    int32_t n, const int32_t* req, const int32_t* tok, void* out,
+                    hipStream_t stream) {
+  const int rc = validate_problem(problem);
+  if (rc) return rc;
+  if (n < 0) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  if (!kv_pages || !page_table || !req || !tok || !out) return MLA_ERR_INVALID_ARG;
+  return mla::launch_gather(problem->d_latent, problem->d_rope, problem->page_size,
+                            problem->max_pages_per_seq, problem->kv_dtype, kv_pages, page_table, n,
+                            req, tok, out, stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported combination";
+    case MLA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MLA_ERR_HIP: return "HIP runtime or launch failure";
+    case MLA_ERR_CHECK: return "checked mode: page id or seq_len out of range";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal interface between the C-ABI layer (mla_api.cpp) and the HIP
+// kernels (mla_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace mla {
+
+enum DType : int32_t { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+// One split-stage launch: every argument already validated on the host.
+struct SplitParams {
+  int32_t B, T, H, Dc, Dr, P, NP, MP;
+  int32_t q_dtype, kv_dtype, out_dtype, causal;
+  int32_t S;                   // chunks per request
+  const void* q_abs;
+  const void* q_rope;
+  const void* kv;
+  const float* kv_scales;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  float scale;
+  bool write_final;            // S == 1: write out/lse directly
+  void* out;                   // [B, T*H, Dc] out_dtype (write_final)
+  float* lse;                  // [B, T*H] or nullptr (write_final)
+  float* part_o;               // [B, S, T*H, Dc] fp32 (!write_final)
+  float* part_lse;             // [B, S, T*H] fp32 (!write_final)
+  bool force_generic;          // run the VALU kernel even where the MFMA one applies
+};
+
+enum class Kernel { kMfmaBf16, kMfmaFp8, kGeneric };
+
+// Which kernel serves this shape (host-side decision, no HIP call).
+Kernel pick_kernel(const SplitParams& p);
+
+hipError_t launch_split(const SplitParams& p, hipStream_t stream);
+
+hipError_t launch_combine(int32_t B, int32_t S, int32_t rows, int32_t Dc, const float* part_o,
+                          const float* part_lse, int32_t out_dtype, void* out, float* lse,
+                          hipStream_t stream);
+
+hipError_t launch_gather(int32_t Dc, int32_t Dr, int32_t P, int32_t MP, int32_t kv_dtype,
+                         const void* kv, const int32_t* page_table, int32_t n,
+                         const int32_t* req, const int32_t* tok, void* out, hipStream_t stream);
+
+}  // namespace mla

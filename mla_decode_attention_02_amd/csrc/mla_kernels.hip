@@ -1,0 +1,817 @@
+// HIP kernels for MLA decode over a paged latent KV cache, written for
+// gfx950 (MI355X, CDNA4).
+//
+// Method (TokenSpeed code-audit article, complete technology list, MLA
+// kernel entries): each token stores one row of 512 latent + 64 rope values
+// that serves as the key of every head and, through its latent part, as the
+// value; a split kernel writes per-chunk fp32 partial results, and a
+// reduction kernel merges them by log-sum-exp rescaling and casts to bf16.
+// The tiled online softmax is the FlashAttention rewrite of the plain
+// softmax ("推理优化" tag page, FlashAttention article: blockwise on-chip
+// accumulation, identical result).
+//
+// Kernels in this file:
+//   mla_split_mfma<FP8, WAVES, STAGES>  the hot path: Dc = 512, Dr = 64,
+//       bf16 queries, bf16 or FP8-E4M3 KV, pages of a multiple of 32 tokens.
+//   mla_split_generic                  any widths / dtypes, VALU only.
+//   mla_combine_kernel                 log-sum-exp merge of split partials.
+//   mla_gather_kernel                  test hook for the page-table loader.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <mutex>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef int intx2 __attribute__((vector_size(8)));
+typedef unsigned uintx4 __attribute__((ext_vector_type(4)));
+typedef unsigned uintx2 __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// ------------------------------------------------------------------ loader
+// Physical row of logical token j of request b: the block table maps the
+// request's logical page j / P to a physical page, and j mod P is the slot in
+// it ("推理优化" tag page, PagedAttention article).  Every kernel resolves
+// rows through this one routine.
+__device__ __forceinline__ int64_t kv_row_index(const int32_t* __restrict__ page_table, int MP,
+                                                int P, int b, int j) {
+  const int page = page_table[(int64_t)b * MP + j / P];
+  return (int64_t)page * P + (j % P);
+}
+
+// Split plan: chunk k of a request of length L, with S chunks, covers
+// [k C, min((k+1) C, L)) where C = P * ceil(ceil(L / S) / P) (page aligned).
+__device__ __forceinline__ void chunk_span(int L, int S, int P, int k, int* cb, int* ce) {
+  const int per = (L + S - 1) / S;
+  const int C = ((per + P - 1) / P) * P;
+  const int64_t b0 = (int64_t)k * C;
+  *cb = (int)(b0 < L ? b0 : L);
+  const int64_t e0 = b0 + C;
+  *ce = (int)(e0 < L ? e0 : L);
+}
+
+// Wavefront-wide reductions (64 lanes) by cross-lane shuffles.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Exchange between the two 32-lane halves of a wave (v_permlane32_swap):
+// returns {own-half value, other-half value} combined by the caller.
+__device__ __forceinline__ float half_swap_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// OCP E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; S.1111.111 is
+// NaN; exponent 0 is subnormal (m * 2^-9).
+__device__ __forceinline__ float e4m3_to_float(uint8_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag;
+  if (e == 15u && m == 7u) return __builtin_nanf("");
+  if (e == 0u)
+    mag = (float)m * (1.0f / 512.0f);
+  else
+    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Eight E4M3 codes (little-endian in two dwords) -> eight bf16 (exact).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(unsigned lo, unsigned hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// ----------------------------------------------------- MFMA tile geometry
+// A tile is 32 consecutive tokens of one page.  In LDS:
+//   latent rows: bf16 -> row r starts at 16 * B(r) bytes with
+//     B(r) = 64 r + 64 (r >> 4) + 4 (r & 3) + 17 ((r >> 2) & 3), rows stored
+//     whole and in order; fp8 -> rows r and r + 16 share a 1056 B block
+//     (r & 15), 512 B each, with 16-byte chunk c at c ^ ((r >> 3) & 1)
+//   rope rows:   r * 128 B (bf16) or r * 64 B (fp8), 16-byte chunks XOR
+//     swizzled by row
+//   scales:      32 fp32 (fp8 only)
+// These placements keep both LDS access patterns free of bank conflicts on a
+// 64-bank LDS -- the QK^T read (16 lanes = 16 rows, one logical 16-byte chunk)
+// and the transposed PV read (bf16: 4 rows x two 32-byte runs per 32 lanes;
+// fp8: 8 rows x 2 chunks) -- and every read address is one base register
+// plus an immediate.  The bf16 rows carry no XOR: the transposed read takes a
+// row's 32 bytes from four lanes that must lie contiguous and in order.
+template <bool FP8>
+struct Tile {
+  static constexpr int kRowBytes = FP8 ? 576 : 1152;  // stored row stride in HBM
+  static constexpr int kLat = FP8 ? 512 : 1024;       // latent bytes per row
+  static constexpr int kRope = FP8 ? 64 : 128;        // rope bytes per row
+  static constexpr int kLatBytes = FP8 ? 16 * 1056 : 16 * 2176;
+  static constexpr int kRopeBytes = 32 * kRope;
+  static constexpr int kScaleBytes = FP8 ? 128 : 0;
+  static constexpr int kStage = kLatBytes + kRopeBytes + kScaleBytes;
+
+  static __device__ __forceinline__ int lat_base(int r) {
+    return FP8 ? ((r & 15) * 1056 + (r >> 4) * 512)
+               : 16 * (64 * r + 64 * (r >> 4) + 4 * (r & 3) + 17 * ((r >> 2) & 3));
+  }
+  static __device__ __forceinline__ int xlat(int r) { return FP8 ? ((r >> 3) & 1) : 0; }
+  static __device__ __forceinline__ int xrope(int r) { return FP8 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
+
+  // Direct HBM -> LDS loads per wave per tile (equal for every wave).
+  template <int WAVES>
+  static constexpr int loads_per_wave() {
+    if (!FP8) return 36 / WAVES;
+    return 16 / WAVES + (WAVES == 4 ? 1 : (WAVES == 2 ? 2 : 3));
+  }
+};
+
+// One 64-lane direct HBM -> LDS load of 16 bytes per lane: lane i reads
+// gbase + voff (gbase wave-uniform) and writes LDS address lds + 16 i.
+// Issued through inline assembly so that the compiler does not guard every
+// later LDS read with a wait for all outstanding loads; the kernel orders
+// them itself with s_waitcnt vmcnt + a workgroup barrier before a stage is
+// read, and a barrier before a stage is refilled.
+__device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform by construction
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(m0v)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(LDS_AS const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// Issue the direct-to-LDS loads of one tile for this wave.  `tile_g` is the
+// first row of the tile in HBM (32 rows, contiguous within one page).
+template <bool FP8, int WAVES>
+__device__ __forceinline__ void issue_tile(const char* tile_g, const float* scale_g,
+                                           LDS_AS char* st, int wave, int lane) {
+  using G = Tile<FP8>;
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int q = 0; q < 32 / WAVES; ++q) {
+      const int r = wave + q * WAVES;
+      const int c = lane ^ G::xlat(r);
+      lds_dma16(tile_g, r * G::kRowBytes + 16 * c, lds_addr(st + G::lat_base(r)));
+    }
+#pragma unroll
+    for (int q = 0; q < 4 / WAVES; ++q) {
+      const int qq = wave + q * WAVES;
+      const int r = 8 * qq + (lane >> 3);
+      const int c = (lane & 7) ^ G::xrope(r);
+      lds_dma16(tile_g, r * G::kRowBytes + G::kLat + 16 * c,
+                lds_addr(st + G::kLatBytes + 1024 * qq));
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 16 / WAVES; ++q) {
+      const int pr = wave + q * WAVES;          // rows pr and pr + 16
+      const int r = pr + 16 * (lane >> 5);
+      const int c = (lane & 31) ^ G::xlat(r);
+      lds_dma16(tile_g, r * G::kRowBytes + 16 * c, lds_addr(st + pr * 1056));
+    }
+    // rope (2 instructions) and scales (1, lanes 0..7), spread so that every
+    // wave issues the same count; duplicate scale loads write the same bytes.
+    constexpr int kExtra = (WAVES == 4 ? 1 : (WAVES == 2 ? 2 : 3));
+#pragma unroll
+    for (int e = 0; e < kExtra; ++e) {
+      int job;  // 0, 1 = rope halves; 2 = scales
+      if (WAVES == 4) job = wave < 2 ? wave : 2;
+      else if (WAVES == 2) job = e == 0 ? wave : 2;
+      else job = e;
+      if (job < 2) {
+        const int r = 16 * job + (lane >> 2);
+        const int c = (lane & 3) ^ G::xrope(r);
+        lds_dma16(tile_g, r * G::kRowBytes + G::kLat + 16 * c,
+                  lds_addr(st + G::kLatBytes + 1024 * job));
+      } else if (lane < 8) {
+        lds_dma16(scale_g, 16 * lane, lds_addr(st + G::kLatBytes + G::kRopeBytes));
+      }
+    }
+  }
+}
+
+// Zero the rows r >= valid of a loaded tile (their slots are past the end of
+// the request and may hold anything, NaN included); called by all threads.
+template <bool FP8, int WAVES>
+__device__ __forceinline__ void zero_tail_rows(LDS_AS char* st, int valid, int tid) {
+  using G = Tile<FP8>;
+  const int nrows = 32 - valid;
+  constexpr int lat_chunks = G::kLat / 16, rope_chunks = G::kRope / 16;
+  for (int x = tid; x < nrows * lat_chunks; x += 64 * WAVES) {
+    const int r = valid + x / lat_chunks, c = x % lat_chunks;
+    *(LDS_AS uintx4*)(st + G::lat_base(r) + 16 * c) = uintx4{0, 0, 0, 0};
+  }
+  for (int x = tid; x < nrows * rope_chunks; x += 64 * WAVES) {
+    const int r = valid + x / rope_chunks, c = x % rope_chunks;
+    *(LDS_AS uintx4*)(st + G::kLatBytes + r * G::kRope + 16 * c) = uintx4{0, 0, 0, 0};
+  }
+  if (FP8)
+    for (int r = valid + tid; r < 32; r += 64 * WAVES)
+      *(LDS_AS float*)(st + G::kLatBytes + G::kRopeBytes + 4 * r) = 0.0f;
+}
+
+// Token slot m of the QK^T A-operand is fed from tile row swap_bits23(m), so
+// that in the MFMA accumulator lane-half h, register i holds tile token
+// 16 (i / 8) + 8 h + (i % 8): eight consecutive tokens per PV step, matching
+// what the transposed LDS reads deliver for the value operand.
+__device__ __forceinline__ int swap_bits23(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Latent/rope dims held by query-fragment kk for lane half h.
+template <bool FP8>
+__device__ __forceinline__ int qfrag_dim(int kk, int h) {
+  return FP8 ? (32 * (kk >> 1) + 16 * h + 8 * (kk & 1)) : (16 * kk + 8 * h);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  // wait until at most `ahead` later tiles' loads (N each) are outstanding
+  switch (ahead) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<N>(); break;
+    case 2: wait_vmcnt<2 * N < 64 ? 2 * N : 0>(); break;
+    default: wait_vmcnt<3 * N < 64 ? 3 * N : 0>(); break;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ T uniform_load(const T* p) {
+  // wave-uniform address: read through the scalar cache
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// ------------------------------------------------------- MFMA split kernel
+// One workgroup = WAVES wavefronts = 32 * WAVES query rows (row r = t * H + h
+// of one request: the query-token fold puts drafts and heads on one axis) over
+// one chunk of one request.  Each wave keeps its 32 query rows in registers
+// as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16, K = the 576-deep
+// dot split in 36 steps), so a row's 32 token scores sit in one lane pair and
+// the softmax max/sum needs one half-swap; then O^T += V^T P^T with the value
+// operand read transposed from the same LDS tile (ds_read_b64_tr_b16 / _b8).
+// O^T for the wave's 32 rows x 512 latent columns is 16 accumulators (256
+// registers per lane).
+template <bool FP8, int WAVES, int STAGES>
+__global__ void __launch_bounds__(64 * WAVES, 1)
+mla_split_mfma(SplitParams p, int groups) {
+  using G = Tile<FP8>;
+  constexpr int kRows = 32 * WAVES;
+  constexpr int kLoads = G::template loads_per_wave<WAVES>();
+  static_assert((STAGES - 1) * kLoads < 64, "vmcnt range");
+  static_assert(STAGES >= 2 && STAGES <= 4, "stage count");
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+  LDS_AS char* smem = (LDS_AS char*)(LDS_AS void*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int h = lane >> 5, n = lane & 31;
+
+  // XCD-aware block mapping: consecutive hardware block ids go to different
+  // XCDs (id mod 8), so the row groups of one (request, chunk) unit are given
+  // ids 8 apart and share that XCD's L2 while they read the same pages.
+  const int x = blockIdx.x;
+  const int xcd = x & 7, slot = x >> 3;
+  const int k8 = slot / groups, g = slot - k8 * groups;
+  const int unit = 8 * k8 + xcd;
+  if (unit >= p.B * p.S) return;
+  const int b = unit / p.S, s = unit - b * p.S;
+
+  const int M = p.T * p.H;
+  const int gr = g * kRows + 32 * wave + n;  // this lane's query row
+  const bool row_ok = gr < M;
+  const int t = row_ok ? gr / p.H : 0;
+
+  const int L = uniform_load(p.seq_lens + b);
+  int cb, ce;
+  chunk_span(L, p.S, p.P, s, &cb, &ce);
+  const int vis = p.causal ? (L - p.T + 1 + t) : L;
+  const int lim = vis < ce ? vis : ce;  // tokens >= lim are masked for this row
+
+  // ---- query fragments (B operand).  Padding rows (gr >= M) reuse row
+  // M - 1: they are computed like any row and never written out.
+  bf16x8 qf[36];
+  {
+    const int64_t qrow = (int64_t)b * M + (row_ok ? gr : M - 1);
+    const __bf16* qa = (const __bf16*)p.q_abs + qrow * 512;
+    const __bf16* qr = (const __bf16*)p.q_rope + qrow * 64;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) qf[kk] = *(const bf16x8*)(qa + qfrag_dim<FP8>(kk, h));
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = *(const bf16x8*)(qr + qfrag_dim<FP8>(kk, h));
+  }
+
+  floatx16 acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = floatx16{};
+  // Softmax reference: p = 2^(z - m_ref) in the log2 domain.  m_ref is the
+  // row maximum of the chunk's first tile and is never moved while
+  // accumulating: any reference within 2^60 of the true maximum keeps every p
+  // and every partial sum finite and normal in fp32/bf16, so O needs no
+  // rescaling.  If a later tile's maximum exceeds m_ref by more than that,
+  // the workgroup restarts the chunk with m_ref = the largest maximum seen
+  // (zeroing the accumulators), which real attention logits never trigger.
+  float m_ref = neg_inf();
+  float m_seen = neg_inf();  // largest tile maximum seen so far
+  float l_part = 0.0f;       // this lane-half's share of the normaliser
+  const float scale_log2 = p.scale * kLog2e;
+  constexpr float kRestartMargin = 60.0f;
+
+  const int ntiles = (ce - cb + 31) >> 5;
+  const char* kv = (const char*)p.kv;
+  const int rho = swap_bits23(n);  // tile row feeding A-operand slot n
+  const int64_t pt_row = (int64_t)b * p.MP;
+
+  auto issue = [&](int i) {
+    const int ts = cb + 32 * i;
+    const int page = uniform_load(p.page_table + pt_row + ts / p.P);
+    const int64_t row0 = (int64_t)page * p.P + (ts % p.P);
+    issue_tile<FP8, WAVES>(kv + row0 * G::kRowBytes, FP8 ? p.kv_scales + row0 : nullptr,
+                           smem + (i % STAGES) * G::kStage, wave, lane);
+  };
+
+  // per-lane LDS read offsets (stage relative)
+  const int k_off = G::lat_base(rho) + 16 * (FP8 ? (h ^ G::xlat(rho)) : 0);
+  const int grp = lane >> 4, sl = lane & 15, dh = grp & 1;
+
+#pragma unroll
+  for (int i = 0; i < STAGES - 1; ++i)
+    if (i < ntiles) issue(i);
+
+  // Wait for tile i, refill the stage freed by tile i - 1, clear past-the-end
+  // rows; returns tile i's stage.
+  auto stage_in = [&](int i) -> LDS_AS char* {
+    const int ahead_tiles = ntiles - 1 - i;
+    wait_ahead<kLoads>(ahead_tiles < STAGES - 2 ? ahead_tiles : STAGES - 2);
+    __syncthreads();
+    if (i + STAGES - 1 < ntiles) issue(i + STAGES - 1);
+    LDS_AS char* st = smem + (i % STAGES) * G::kStage;
+    const int ts = cb + 32 * i;
+    if (ts + 32 > L) {  // last tile of the request: clear slots past its end
+      zero_tail_rows<FP8, WAVES>(st, L - ts, tid);
+      __syncthreads();
+    }
+    return st;
+  };
+
+  // S^T = K Q^T for one tile (32 tokens x 32 rows), then scaled (log2
+  // domain) and masked in place; returns the row maximum over the tile.
+  auto scores = [&](LDS_AS char* st, int ts, floatx16& sacc) -> float {
+    sacc = floatx16{};
+    if constexpr (!FP8) {
+      const LDS_AS char* rowp = st + k_off + 16 * h;
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk) {
+        const bf16x8 a = *(const LDS_AS bf16x8*)(rowp + 32 * kk);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc, 0, 0, 0);
+      }
+      const LDS_AS char* ropep = st + G::kLatBytes + rho * G::kRope;
+      const int swr = G::xrope(rho);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 a = *(const LDS_AS bf16x8*)(ropep + 16 * ((2 * kk + h) ^ swr));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[32 + kk], sacc, 0, 0, 0);
+      }
+    } else {
+      const LDS_AS char* rowp = st + k_off;
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const uintx4 raw = *(const LDS_AS uintx4*)(rowp + 32 * kk);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16(raw[0], raw[1]),
+                                                        qf[2 * kk], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16(raw[2], raw[3]),
+                                                        qf[2 * kk + 1], sacc, 0, 0, 0);
+      }
+      const LDS_AS char* ropep = st + G::kLatBytes + rho * G::kRope;
+      const int swr = G::xrope(rho);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uintx4 raw = *(const LDS_AS uintx4*)(ropep + 16 * ((2 * kk + h) ^ swr));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16(raw[0], raw[1]),
+                                                        qf[32 + 2 * kk], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16(raw[2], raw[3]),
+                                                        qf[33 + 2 * kk], sacc, 0, 0, 0);
+      }
+    }
+    const LDS_AS float* tsc = (const LDS_AS float*)(st + G::kLatBytes + G::kRopeBytes);
+    const int lim_rel = lim - ts;
+    float mx = neg_inf();
+#pragma unroll
+    for (int i2 = 0; i2 < 16; ++i2) {
+      const int tok = 16 * (i2 >> 3) + 8 * h + (i2 & 7);
+      float v = sacc[i2];
+      if constexpr (FP8) v *= tsc[tok];
+      v *= scale_log2;
+      sacc[i2] = tok < lim_rel ? v : neg_inf();
+      mx = fmaxf(mx, sacc[i2]);
+    }
+    return half_swap_max(mx);
+  };
+
+  // p = 2^(z - m_ref) -> bf16 value-operand weights (FP8: times the row
+  // scale); O^T += V^T P^T with V^T read transposed from the latent tile.
+  auto accumulate = [&](LDS_AS char* st, const floatx16& z) {
+    const LDS_AS float* tsc = (const LDS_AS float*)(st + G::kLatBytes + G::kRopeBytes);
+    const float mu = m_ref == neg_inf() ? 0.0f : m_ref;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // the normaliser sums the weights exactly as the PV product sees them
+        const __bf16 wb = (__bf16)fast_exp2(z[8 * q + j] - mu);
+        l_part += (float)wb;
+        if constexpr (FP8)
+          pb[q][j] = (__bf16)((float)wb * tsc[16 * q + 8 * h + j]);
+        else
+          pb[q][j] = wb;
+      }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if constexpr (!FP8) {
+        const int r0 = 16 * q + 8 * h + (sl >> 2);
+        const int r1 = r0 + 4;
+        const int cpart = 2 * dh + ((sl & 3) >> 1);
+        const LDS_AS char* b0p = st + G::lat_base(r0) + 16 * cpart + 8 * (sl & 1);
+        const LDS_AS char* b1p = st + G::lat_base(r1) + 16 * cpart + 8 * (sl & 1);
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+          const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(b0p + 64 * db));
+          const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(b1p + 64 * db));
+          // whole-vector reinterpretation: element-wise bf16 inserts were
+          // miscompiled into a broadcast of element 0
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[q], acc[db], 0, 0, 0);
+        }
+      } else {
+        const int r0 = 16 * q + 8 * h + (sl >> 1);
+        const LDS_AS char* bp = st + G::lat_base(r0) + 16 * (dh ^ G::xlat(r0)) + 8 * (sl & 1);
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+          const intx2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS intx2*)(bp + 32 * db));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              e4m3x8_to_bf16((unsigned)v[0], (unsigned)v[1]), pb[q], acc[db], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // Restart requests, one word per tile in a ring of three (after the
+  // pipeline stages): lanes write word i % 3 while handling tile i; every wave
+  // reads it after the barrier that opens tile i + 1 (so all waves see the
+  // same value and leave the loop together), and it is cleared after the
+  // barrier of tile i + 2, before tile i + 3 can write it again.
+  volatile LDS_AS int* req = (volatile LDS_AS int*)(smem + STAGES * G::kStage);
+  if (tid < 3) req[tid] = 0;  // ordered before any use by the first tile barrier
+
+  for (;;) {
+    bool restart = false;
+    int w_cur = 0, w_prev = 2, w_old = 1;  // i % 3, (i - 1) % 3, (i - 2) % 3
+    for (int i = 0; i < ntiles; ++i) {
+      LDS_AS char* st = stage_in(i);
+      if (i >= 1 && req[w_prev]) {
+        restart = true;
+        break;
+      }
+      if (i >= 2 && tid == 0) req[w_old] = 0;
+      floatx16 z;
+      const float mx = scores(st, cb + 32 * i, z);
+      m_seen = fmaxf(m_seen, mx);
+      if (m_ref == neg_inf()) m_ref = mx;  // first visible tile of this row
+      if (mx > m_ref + kRestartMargin) req[w_cur] = 1;
+      accumulate(st, z);
+      w_old = w_prev;
+      w_prev = w_cur;
+      w_cur = w_cur == 2 ? 0 : w_cur + 1;
+    }
+    if (!restart && ntiles > 0) {  // the last tile may have asked for a restart too
+      __syncthreads();
+      restart = req[w_prev] != 0;
+    }
+    if (!restart) break;
+    // Rare path: drain the pipeline, reset, and run the chunk again.
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (tid < 3) req[tid] = 0;
+    m_ref = m_seen;
+    l_part = 0.0f;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) acc[db] = floatx16{};
+#pragma unroll
+    for (int i = 0; i < STAGES - 1; ++i)
+      if (i < ntiles) issue(i);
+  }
+
+  // ---- epilogue: normalise and write (lane pair n, n+32 shares row gr)
+  const float l_tot = half_swap_sum(l_part);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse_v = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : neg_inf();
+  if (!row_ok) return;
+  if (p.write_final) {
+    const int64_t obase = ((int64_t)b * M + gr) * 512;
+#pragma unroll
+    for (int db = 0; db < 16; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * db + 8 * g4 + 4 * h;
+        const float o0 = acc[db][4 * g4 + 0] * inv, o1 = acc[db][4 * g4 + 1] * inv;
+        const float o2 = acc[db][4 * g4 + 2] * inv, o3 = acc[db][4 * g4 + 3] * inv;
+        if (p.out_dtype == kBF16) {
+          *(bf16x4*)((__bf16*)p.out + obase + d) = bf16x4{(__bf16)o0, (__bf16)o1, (__bf16)o2, (__bf16)o3};
+        } else {
+          *(floatx4*)((float*)p.out + obase + d) = floatx4{o0, o1, o2, o3};
+        }
+      }
+    if (p.lse && h == 0) p.lse[(int64_t)b * M + gr] = lse_v;
+  } else {
+    const int64_t prow = ((int64_t)b * p.S + s) * M + gr;
+    float* po = p.part_o + prow * 512;
+#pragma unroll
+    for (int db = 0; db < 16; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * db + 8 * g4 + 4 * h;
+        *(floatx4*)(po + d) = floatx4{acc[db][4 * g4 + 0] * inv, acc[db][4 * g4 + 1] * inv,
+                                      acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv};
+      }
+    if (h == 0) p.part_lse[prow] = lse_v;
+  }
+}
+
+// ---------------------------------------------------- generic split kernel
+// Any widths and dtypes, VALU only: one wavefront per query row, 64 tokens at
+// a time (lane j scores token j), online softmax with wavefront reductions,
+// then the latent accumulation with each lane owning columns lane + 64 k.
+constexpr int kGenericMaxDc = 1024;
+
+__device__ __forceinline__ float kv_value(const SplitParams& p, int64_t row, int d) {
+  const int D = p.Dc + p.Dr;
+  const int64_t i = row * D + d;
+  if (p.kv_dtype == kF32) return ((const float*)p.kv)[i];
+  if (p.kv_dtype == kBF16) return bf16_bits_to_float(((const uint16_t*)p.kv)[i]);
+  return e4m3_to_float(((const uint8_t*)p.kv)[i]) * p.kv_scales[row];
+}
+
+__device__ __forceinline__ float q_value(const SplitParams& p, const void* base, int64_t i) {
+  return p.q_dtype == kF32 ? ((const float*)base)[i] : bf16_bits_to_float(((const uint16_t*)base)[i]);
+}
+
+__global__ void __launch_bounds__(256) mla_split_generic(SplitParams p) {
+  extern __shared__ float gsm[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int M = p.T * p.H, D = p.Dc + p.Dr;
+  const int gr = blockIdx.x * 4 + wave;
+  const int s = blockIdx.y, b = blockIdx.z;
+  if (gr >= M) return;
+  float* q = gsm + wave * D;
+  for (int d = lane; d < p.Dc; d += 64) q[d] = q_value(p, p.q_abs, ((int64_t)b * M + gr) * p.Dc + d);
+  for (int e = lane; e < p.Dr; e += 64) q[p.Dc + e] = q_value(p, p.q_rope, ((int64_t)b * M + gr) * p.Dr + e);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+
+  const int t = gr / p.H;
+  const int L = p.seq_lens[b];
+  int cb, ce;
+  chunk_span(L, p.S, p.P, s, &cb, &ce);
+  const int vis = p.causal ? (L - p.T + 1 + t) : L;
+  const int lim = vis < ce ? vis : ce;
+  const float scale_log2 = p.scale * kLog2e;
+  constexpr int kPer = kGenericMaxDc / 64;
+  float acc[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) acc[k] = 0.0f;
+  float m = neg_inf(), l = 0.0f;
+  for (int j0 = cb; j0 < lim; j0 += 64) {
+    const int j = j0 + lane;
+    const bool ok = j < lim;
+    const int64_t row = ok ? kv_row_index(p.page_table, p.MP, p.P, b, j) : 0;
+    float z = neg_inf();
+    if (ok) {
+      float dot = 0.0f;
+      for (int d = 0; d < D; ++d) dot += q[d] * kv_value(p, row, d);
+      z = dot * scale_log2;
+    }
+    const float mx = wave_max(z);
+    const float m_new = fmaxf(m, mx);
+    const float alpha = m == neg_inf() ? 0.0f : fast_exp2(m - m_new);
+    const float pj = ok ? fast_exp2(z - m_new) : 0.0f;
+    l = l * alpha + wave_sum(pj);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) acc[k] *= alpha;
+    m = m_new;
+    const int cnt = lim - j0 < 64 ? lim - j0 : 64;
+    for (int jj = 0; jj < cnt; ++jj) {
+      const float w = __shfl(pj, jj, 64);
+      const int64_t r = ((int64_t)__shfl((int)(row >> 32), jj, 64) << 32) |
+                        (uint32_t)__shfl((int)(row & 0xffffffff), jj, 64);
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int d = lane + 64 * k;
+        if (d < p.Dc) acc[k] += w * kv_value(p, r, d);
+      }
+    }
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const float lse_v = l > 0.0f ? (m + __log2f(l)) * kLn2 : neg_inf();
+  if (p.write_final) {
+    const int64_t ob = ((int64_t)b * M + gr) * p.Dc;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int d = lane + 64 * k;
+      if (d < p.Dc) {
+        if (p.out_dtype == kBF16) ((__bf16*)p.out)[ob + d] = (__bf16)(acc[k] * inv);
+        else ((float*)p.out)[ob + d] = acc[k] * inv;
+      }
+    }
+    if (p.lse && lane == 0) p.lse[(int64_t)b * M + gr] = lse_v;
+  } else {
+    const int64_t prow = ((int64_t)b * p.S + s) * M + gr;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int d = lane + 64 * k;
+      if (d < p.Dc) p.part_o[prow * p.Dc + d] = acc[k] * inv;
+    }
+    if (lane == 0) p.part_lse[prow] = lse_v;
+  }
+}
+
+// ----------------------------------------------------------- combine kernel
+// One wavefront per (request, row): weights w_k = exp(lse_k - max lse),
+// out = sum_k w_k o_k / sum_k w_k; chunks with lse = -inf are skipped (their
+// partial rows are never read).
+__global__ void __launch_bounds__(256)
+mla_combine_kernel(int B, int S, int rows, int Dc, const float* __restrict__ po,
+                   const float* __restrict__ pl, int out_dtype, void* out, float* lse) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + wave;
+  if (idx >= (int64_t)B * rows) return;
+  const int b = (int)(idx / rows), r = (int)(idx - (int64_t)b * rows);
+  float mx = neg_inf();
+  for (int k = lane; k < S; k += 64) mx = fmaxf(mx, pl[((int64_t)b * S + k) * rows + r]);
+  mx = wave_max(mx);
+  float wsum = 0.0f;
+  for (int k = lane; k < S; k += 64) {
+    const float v = pl[((int64_t)b * S + k) * rows + r];
+    wsum += v == neg_inf() ? 0.0f : fast_exp2((v - mx) * kLog2e);
+  }
+  wsum = wave_sum(wsum);
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  const int64_t ob = idx * Dc;
+  if ((Dc & 3) == 0) {
+    for (int d = 4 * lane; d < Dc; d += 256) {
+      floatx4 a = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int k = 0; k < S; ++k) {
+        const int64_t pr = ((int64_t)b * S + k) * rows + r;
+        const float v = pl[pr];
+        if (v == neg_inf()) continue;
+        const float w = fast_exp2((v - mx) * kLog2e);
+        a += w * *(const floatx4*)(po + pr * Dc + d);
+      }
+      a *= inv;
+      if (out_dtype == kBF16)
+        *(bf16x4*)((__bf16*)out + ob + d) = bf16x4{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]};
+      else
+        *(floatx4*)((float*)out + ob + d) = a;
+    }
+  } else {
+    for (int d = lane; d < Dc; d += 64) {
+      float a = 0.0f;
+      for (int k = 0; k < S; ++k) {
+        const int64_t pr = ((int64_t)b * S + k) * rows + r;
+        const float v = pl[pr];
+        if (v == neg_inf()) continue;
+        a += fast_exp2((v - mx) * kLog2e) * po[pr * Dc + d];
+      }
+      a *= inv;
+      if (out_dtype == kBF16) ((__bf16*)out)[ob + d] = (__bf16)a;
+      else ((float*)out)[ob + d] = a;
+    }
+  }
+  if (lse && lane == 0) lse[idx] = wsum > 0.0f ? mx + __logf(wsum) : neg_inf();
+}
+
+// ------------------------------------------------------------ gather hook
+__global__ void mla_gather_kernel(int D, int elt, int P, int MP, const char* __restrict__ kv,
+                                  const int32_t* __restrict__ page_table, int n,
+                                  const int32_t* __restrict__ req, const int32_t* __restrict__ tok,
+                                  char* __restrict__ out) {
+  const int rb = D * elt;
+  const int64_t total = (int64_t)n * rb;
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < total;
+       x += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(x / rb), byte = (int)(x - (int64_t)i * rb);
+    const int64_t row = kv_row_index(page_table, MP, P, req[i], tok[i]);
+    out[x] = kv[row * rb + byte];
+  }
+}
+
+// ------------------------------------------------------------- launchers
+template <bool FP8, int WAVES, int STAGES>
+hipError_t launch_mfma(const SplitParams& p, hipStream_t stream) {
+  constexpr int kRows = 32 * WAVES;
+  const int M = p.T * p.H;
+  const int groups = (M + kRows - 1) / kRows;
+  const int units = p.B * p.S;
+  const int64_t blocks = 8LL * groups * ((units + 7) / 8);
+  const size_t lds = (size_t)STAGES * Tile<FP8>::kStage + 16;  // + restart request ring
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute((const void*)mla_split_mfma<FP8, WAVES, STAGES>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((mla_split_mfma<FP8, WAVES, STAGES>), dim3((unsigned)blocks), dim3(64 * WAVES),
+                     lds, stream, p, groups);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+Kernel pick_kernel(const SplitParams& p) {
+  if (p.force_generic) return Kernel::kGeneric;
+  const bool mfma_shape = p.Dc == 512 && p.Dr == 64 && p.q_dtype == kBF16 && p.P % 32 == 0 &&
+                          (p.kv_dtype == kBF16 || p.kv_dtype == kFP8);
+  if (!mfma_shape) return Kernel::kGeneric;
+  return p.kv_dtype == kFP8 ? Kernel::kMfmaFp8 : Kernel::kMfmaBf16;
+}
+
+hipError_t launch_split(const SplitParams& p, hipStream_t stream) {
+  switch (pick_kernel(p)) {
+    case Kernel::kMfmaBf16: return launch_mfma<false, 4, 4>(p, stream);
+    case Kernel::kMfmaFp8: return launch_mfma<true, 4, 4>(p, stream);
+    default: break;
+  }
+  const int M = p.T * p.H;
+  if (p.B == 0 || M == 0) return hipSuccess;
+  dim3 grid((unsigned)((M + 3) / 4), (unsigned)p.S, (unsigned)p.B);
+  const size_t lds = sizeof(float) * 4 * (size_t)(p.Dc + p.Dr);
+  hipLaunchKernelGGL(mla_split_generic, grid, dim3(256), lds, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(int32_t B, int32_t S, int32_t rows, int32_t Dc, const float* part_o,
+                          const float* part_lse, int32_t out_dtype, void* out, float* lse,
+                          hipStream_t stream) {
+  const int64_t n = (int64_t)B * rows;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream, B, S,
+                     rows, Dc, part_o, part_lse, out_dtype, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(int32_t Dc, int32_t Dr, int32_t P, int32_t MP, int32_t kv_dtype,
+                         const void* kv, const int32_t* page_table, int32_t n, const int32_t* req,
+                         const int32_t* tok, void* out, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int elt = kv_dtype == kF32 ? 4 : (kv_dtype == kBF16 ? 2 : 1);
+  const int64_t total = (int64_t)n * (Dc + Dr) * elt;
+  const int64_t blocks64 = (total + 255) / 256;
+  const unsigned blocks = (unsigned)(blocks64 < 4096 ? blocks64 : 4096);
+  hipLaunchKernelGGL(mla_gather_kernel, dim3(blocks), dim3(256), 0, stream, Dc + Dr, elt, P, MP,
+                     (const char*)kv, page_table, n, req, tok, (char*)out);
+  return hipGetLastError();
+}
+
+}  // namespace mla
