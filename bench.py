@@ -1,0 +1,319 @@
+"""Benchmark: MLA decode over a paged latent KV cache on one MI355X.
+
+One step = one full decode of one batch (split kernel + log-sum-exp merge,
+the two launches ``mla_decode`` makes) on synthetic inputs already resident
+in HBM.  Steps rotate over several copies of the KV pool and queries (one per
+"layer") so that the 256 MB last-level cache never serves a step from the
+previous one.  Prints ONE JSON line (see the ``print`` at the end).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import synth  # noqa: E402
+
+METRIC = "MLA decode KV GB/s + tokens/s per GPU; % of HBM/MFMA roofline (1 MI355X)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+LLC_BYTES = 256 << 20          # MI355X Infinity Cache
+
+
+def algorithmic(w, seq_lens, with_output):
+    """Bytes and MFMA flops the decode must touch/do, per the method's data:
+    each token's stored row once (a prefix shared by all requests once), the
+    queries, the page-table entries and lengths, and the output if written."""
+    L = np.asarray(seq_lens, dtype=np.int64)
+    row = {"bf16": 2 * w.d, "fp8": w.d + 4, "f32": 4 * w.d}[w.kv_dtype]
+    kv_logical = int(L.sum()) * row
+    kv_unique = kv_logical - max(0, w.batch - 1) * w.shared_prefix * row
+    q_bytes = w.batch * w.rows * w.d * (2 if w.q_dtype == "bf16" else 4)
+    out_bytes = w.batch * w.rows * w.d_latent * (2 if w.out_dtype == "bf16" else 4)
+    table = int(np.ceil(L / w.page_size).sum()) * 4 + 4 * w.batch
+    bytes_ = kv_unique + q_bytes + table + (out_bytes if with_output else 0)
+    flops = 2 * w.heads * w.q_len * int(L.sum()) * (w.d + w.d_latent)
+    return {"bytes": bytes_, "kv_logical": kv_logical, "kv_unique": kv_unique, "flops": flops}
+
+
+def device_inputs(inp, copies):
+    """Host synth arrays -> `copies` independent device copies of KV and queries."""
+    w = inp["workload"]
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    base = {k: t(inp[k]) for k in ("q_abs", "q_rope", "kv", "page_table", "seq_lens")}
+    base["kv_scales"] = None if inp["kv_scales"] is None else t(inp["kv_scales"])
+    sets = [base]
+    for _ in range(copies - 1):
+        c = dict(base)
+        for k in ("q_abs", "q_rope", "kv", "kv_scales"):
+            if base[k] is not None:
+                c[k] = base[k].clone()
+        sets.append(c)
+    del w
+    return sets
+
+
+def cpu_baseline(inp, budget_s):
+    """Time the fp64 CPU oracle on a bounded sample of the workload's requests."""
+    import oracle
+    w = inp["workload"]
+    L = inp["seq_lens"]
+    threads = oracle.max_threads()
+    # calibrate on the shortest request, then take requests until ~budget
+    probe = [int(np.argmin(L))]
+    t0 = time.perf_counter()
+    oracle.attend(inp, req_ids=probe)
+    per_token = (time.perf_counter() - t0) / max(1, int(L[probe[0]]))
+    pick, est = [], 0.0
+    for b in np.random.default_rng(7).permutation(w.batch):
+        if est + per_token * int(L[b]) > budget_s and pick:
+            break
+        pick.append(int(b))
+        est += per_token * int(L[b])
+    t0 = time.perf_counter()
+    oracle.attend(inp, req_ids=pick)
+    dt = time.perf_counter() - t0
+    sub = algorithmic(w, L[pick], with_output=True)
+    return {
+        "value": round(sub["kv_logical"] / dt / 1e9, 4), "unit": "GB/s",
+        "tokens_per_s": round(len(pick) * w.q_len / dt, 3),
+        "cores": threads, "kind": "oracle",
+        "sample": f"{len(pick)} of {w.batch} requests ({int(L[pick].sum())} KV tokens, all "
+                  f"{w.heads} heads x {w.q_len} query tokens), fp64 C oracle, {dt:.1f} s",
+    }
+
+
+KERNEL_SOURCE = os.path.join(ROOT, "mla_decode_attention_02_amd", "csrc", "mla_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def pmc_summary(pmc_dir, workload, calib_mib, out_path):
+    """Per-launch HBM traffic of the split kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the calibration copy of calib_mib MiB in the same run."""
+    import csv
+    import glob
+
+    def per_kernel(counter):
+        rows = []
+        for f in glob.glob(os.path.join(pmc_dir, "*counter_collection.csv")):
+            rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        split = [float(r["Counter_Value"]) for r in rows if "mla_split" in r["Kernel_Name"]]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        return split, copies
+
+    f_split, f_copy = per_kernel("FETCH_SIZE")
+    w_split, w_copy = per_kernel("WRITE_SIZE")
+    calib_kib = calib_mib * 1024.0
+    rf = calib_kib / max(f_copy)
+    wf = calib_kib / max(w_copy)
+    fetch = float(np.mean(f_split)) * rf * 1024
+    write = float(np.mean(w_split)) * wf * 1024
+    lines = [
+        f"# HBM traffic of mla_split_mfma, workload {workload}",
+        "",
+        f"kernel_source_sha256_16: {kernel_source_hash()}",
+        f"dispatches: {len(f_split)} (FETCH_SIZE run), {len(w_split)} (WRITE_SIZE run)",
+        f"FETCH_SIZE per dispatch (KiB, raw): {np.mean(f_split):.1f}",
+        f"WRITE_SIZE per dispatch (KiB, raw): {np.mean(w_split):.1f}",
+        f"calibration copy {calib_mib} MiB: FETCH_SIZE {max(f_copy):.1f} KiB -> x{rf:.4f}, "
+        f"WRITE_SIZE {max(w_copy):.1f} KiB -> x{wf:.4f}",
+        f"read_bytes_per_launch: {fetch:.0f}",
+        f"write_bytes_per_launch: {write:.0f}",
+        f"traffic_bytes_per_launch: {fetch + write:.0f}",
+    ]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def recorded_traffic(workload):
+    """Traffic per launch recorded for this workload, if taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"mla_split_mfma__{workload}__traffic.md")
+    if not os.path.exists(path):
+        return None
+    info = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            info[k.strip()] = v.strip()
+    if info.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return int(float(info["traffic_bytes_per_launch"]))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="deepseek_v3_bf16",
+                    choices=[w.name for w in synth.WORKLOADS])
+    ap.add_argument("--num-splits", type=int, default=-1,
+                    help="override the split count (default: the workload's, else the library's)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--pmc-summary", metavar="DIR",
+                    help="summarise FETCH_SIZE/WRITE_SIZE rocprofv3 CSVs in DIR and exit")
+    ap.add_argument("--pmc-out", metavar="FILE", help="where --pmc-summary writes its summary")
+    args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, args.workload, args.calib_copy_mib or 1024,
+                    args.pmc_out or os.path.join(PROFILES, f"mla_split_mfma__{args.workload}__traffic.md"))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the decode on a single MI355X "
+              "(--gpus 1); multi-GPU runs are not part of it.", file=sys.stderr)
+        sys.exit(2)
+    import mla_decode_attention_02_amd as mla
+    mla.library()
+    torch.cuda.set_device(0)
+
+    w = next(x for x in synth.WORKLOADS if x.name == args.workload)
+    inp = synth.make_inputs(w, poison=False)
+    kv_bytes = inp["kv"].nbytes + (0 if inp["kv_scales"] is None else inp["kv_scales"].nbytes)
+    copies = max(2, min(8, math.ceil(4 * LLC_BYTES / kv_bytes)))
+    sets = device_inputs(inp, copies)
+    d0 = sets[0]
+    S_req = w.num_splits if args.num_splits < 0 else args.num_splits
+    pr = mla.make_problem(d0["q_abs"], d0["q_rope"], d0["kv"], d0["page_table"],
+                          causal=w.causal, num_splits=S_req, max_seq_len=w.max_seq_len)
+    S = mla.num_splits(pr)
+    B, T, H, Dc = d0["q_abs"].shape
+    R = T * H
+    out_dt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+    part_o = torch.empty((B, S, R, Dc), dtype=torch.float32, device="cuda")
+    part_l = torch.empty((B, S, R), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, R, Dc), dtype=out_dt, device="cuda")
+    lse = torch.empty((B, R), dtype=torch.float32, device="cuda")
+    scale = float(inp["scale"])
+
+    # Arguments are marshalled once per KV copy, so that the timed loop only
+    # makes the two C-ABI calls (the same two launches mla_decode makes) and
+    # records the HIP events around them on the launch stream.
+    import ctypes
+    lib = mla.library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    prs = mla.make_problem(d0["q_abs"], d0["q_rope"], d0["kv"], d0["page_table"],
+                           causal=w.causal, num_splits=S, max_seq_len=w.max_seq_len)
+    split_args = [(ctypes.byref(prs), P(d["q_abs"]), P(d["q_rope"]), P(d["kv"]),
+                   P(d["kv_scales"]), P(d["page_table"]), P(d["seq_lens"]),
+                   ctypes.c_float(scale), S, P(part_o), P(part_l), stream) for d in sets]
+    comb_args = (B, S, R, Dc, P(part_o), P(part_l),
+                 mla.MLA_DTYPE_BF16 if out_dt == torch.bfloat16 else mla.MLA_DTYPE_F32,
+                 P(out), P(lse), stream)
+    ws = torch.empty(max(1, mla.workspace_size(prs)), dtype=torch.uint8, device="cuda")
+    dec_args = [(ctypes.byref(prs), P(d["q_abs"]), P(d["q_rope"]), P(d["kv"]),
+                 P(d["kv_scales"]), P(d["page_table"]), P(d["seq_lens"]), ctypes.c_float(scale),
+                 P(out), P(lse), P(ws), ws.numel(), stream) for d in sets]
+
+    def step(i, evs=None):
+        if evs is not None:
+            evs[0].record()
+        if S == 1:
+            rc = lib.mla_decode(*dec_args[i % copies])
+            if evs is not None:
+                evs[1].record()
+        else:
+            rc = lib.mla_decode_split(*split_args[i % copies])
+            if evs is not None:
+                evs[1].record()
+            rc |= lib.mla_combine(*comb_args)
+        if evs is not None:
+            evs[2].record()
+        if rc:
+            raise RuntimeError(f"decode failed: {mla.status_string(rc)}")
+
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    split_ms = [e[0].elapsed_time(e[1]) for e in events]
+    comb_ms = [e[1].elapsed_time(e[2]) for e in events]
+    ms_per_step = wall * 1e3 / args.steps
+
+    L = inp["seq_lens"]
+    alg_split = algorithmic(w, L, with_output=(S == 1))
+    alg_path = algorithmic(w, L, with_output=True)
+    split_avg = float(np.mean(split_ms))
+    tokens_per_s = B * T / (ms_per_step / 1e3)
+    kv_gbs = alg_path["kv_logical"] / (ms_per_step / 1e3) / 1e9
+    t_hbm = alg_path["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = alg_path["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    if bound == "hbm":
+        achieved = alg_split["bytes"] / (split_avg / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = alg_split["flops"] / (split_avg / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    traffic = recorded_traffic(w.name)
+    roof["traffic"] = traffic
+    roof["kernel"] = "mla_split_mfma" if w.d_latent == 512 else "mla_split_generic"
+    roof["per_launch_algorithmic"] = alg_split["bytes"] if bound == "hbm" else alg_split["flops"]
+    roof["kernel_avg_ms"] = round(split_avg, 5)
+    roof["path_roofline_ms"] = round(max(t_hbm, t_mfma) * 1e3, 5)
+    roof["path_frac"] = round(max(t_hbm, t_mfma) * 1e3 / ms_per_step, 4)
+
+    cpu = None if args.no_cpu else cpu_baseline(inp, args.cpu_budget)
+    seq_desc = (f"U[{w.seq_lens[1]},{w.seq_lens[2]}]" if w.seq_lens[0] == "uniform"
+                else f"fixed {w.seq_lens[1][0]}") + f" seed {1000 + w.index}"
+    line = {
+        "metric": METRIC, "value": round(kv_gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 KV, bf16 MFMA", "f32": "f32"}[w.kv_dtype],
+        "data": "synthetic (seeded N(0,1)*sigma rows and queries, random page permutation)",
+        "config": {"workload": w.name, "batch": B, "q_len": T, "heads": H, "d_latent": w.d_latent,
+                   "d_rope": w.d_rope, "page_size": w.page_size, "seq_lens": seq_desc,
+                   "shared_prefix": w.shared_prefix, "causal": w.causal, "num_splits": S,
+                   "kv_copies_rotated": copies, "parallelism": "single GPU"},
+        "tokens_per_s": round(tokens_per_s, 1),
+        "kv_gbs_unique": round(alg_path["kv_unique"] / (ms_per_step / 1e3) / 1e9, 2),
+        "split_ms": round(split_avg, 5), "combine_ms": round(float(np.mean(comb_ms)), 5),
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

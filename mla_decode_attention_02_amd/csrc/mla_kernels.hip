@@ -340,6 +340,10 @@ mla_split_mfma(SplitParams p, int groups) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = *(const bf16x8*)(qr + qfrag_dim<FP8>(kk, h));
   }
+  // Settle the query loads here, once: otherwise the compiler guards their
+  // first use inside the tile loop with vector-memory waits that would also
+  // wait for every tile prefetch in flight.
+  wait_vmcnt<0>();
 
   floatx16 acc[16];
 #pragma unroll
@@ -397,22 +401,42 @@ mla_split_mfma(SplitParams p, int groups) {
   // S^T = K Q^T for one tile (32 tokens x 32 rows), then scaled (log2
   // domain) and masked in place; returns the row maximum over the tile.
   auto scores = [&](LDS_AS char* st, int ts, floatx16& sacc) -> float {
-    sacc = floatx16{};
+    // Two independent accumulation chains (even / odd k-steps): a single
+    // dependent chain issues one MFMA per ~44 cycles instead of ~32.
     if constexpr (!FP8) {
+      floatx16 s0 = floatx16{}, s1 = floatx16{};
       const LDS_AS char* rowp = st + k_off + 16 * h;
-#pragma unroll
-      for (int kk = 0; kk < 32; ++kk) {
-        const bf16x8 a = *(const LDS_AS bf16x8*)(rowp + 32 * kk);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc, 0, 0, 0);
-      }
       const LDS_AS char* ropep = st + G::kLatBytes + rho * G::kRope;
       const int swr = G::xrope(rho);
+      auto kaddr = [&](int kk) -> const LDS_AS bf16x8* {
+        return kk < 32 ? (const LDS_AS bf16x8*)(rowp + 32 * kk)
+                       : (const LDS_AS bf16x8*)(ropep + 16 * ((2 * (kk - 32) + h) ^ swr));
+      };
+      constexpr int kAhead = 4;  // LDS reads in flight ahead of the MFMA using them
+      bf16x8 ring[kAhead];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a = *(const LDS_AS bf16x8*)(ropep + 16 * ((2 * kk + h) ^ swr));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[32 + kk], sacc, 0, 0, 0);
+      for (int kk = 0; kk < kAhead; ++kk) ring[kk] = *kaddr(kk);
+#pragma unroll
+      for (int kk = 0; kk < 36; ++kk) {
+        const bf16x8 a = ring[kk % kAhead];
+        if (kk + kAhead < 36) ring[kk % kAhead] = *kaddr(kk + kAhead);
+        if (kk & 1)
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s1, 0, 0, 0);
+        else
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s0, 0, 0, 0);
       }
+#pragma unroll
+      for (int kk = 0; kk < kAhead; ++kk) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int kk = 0; kk < 36 - kAhead; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int kk = 0; kk < kAhead; ++kk) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      sacc = s0 + s1;
     } else {
+      sacc = floatx16{};
       const LDS_AS char* rowp = st + k_off;
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) {
@@ -474,15 +498,32 @@ mla_split_mfma(SplitParams p, int groups) {
         const int cpart = 2 * dh + ((sl & 3) >> 1);
         const LDS_AS char* b0p = st + G::lat_base(r0) + 16 * cpart + 8 * (sl & 1);
         const LDS_AS char* b1p = st + G::lat_base(r1) + 16 * cpart + 8 * (sl & 1);
-#pragma unroll
-        for (int db = 0; db < 16; ++db) {
+        // whole-vector reinterpretation of the two transposed reads
+        // (element-wise bf16 inserts were miscompiled into a broadcast)
+        auto vread = [&](int db) -> bf16x8 {
           const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(b0p + 64 * db));
           const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(b1p + 64 * db));
-          // whole-vector reinterpretation: element-wise bf16 inserts were
-          // miscompiled into a broadcast of element 0
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        constexpr int kAhead = 3;  // value operands in flight ahead of their MFMA
+        bf16x8 ring[kAhead];
+#pragma unroll
+        for (int db = 0; db < kAhead; ++db) ring[db] = vread(db);
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+          const bf16x8 a = ring[db % kAhead];
+          if (db + kAhead < 16) ring[db % kAhead] = vread(db + kAhead);
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[q], acc[db], 0, 0, 0);
         }
+#pragma unroll
+        for (int db = 0; db < kAhead; ++db) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int db = 0; db < 16 - kAhead; ++db) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int db = 0; db < kAhead; ++db) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       } else {
         const int r0 = 16 * q + 8 * h + (sl >> 1);
         const LDS_AS char* bp = st + G::lat_base(r0) + 16 * (dh ^ G::xlat(r0)) + 8 * (sl & 1);
