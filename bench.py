@@ -123,6 +123,17 @@ def pmc_summary(pmc_dir, workload, calib_mib, out_path):
         copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         return split, copies
 
+    # the kernel-source hash the profiled runs printed in their JSON lines
+    # (their logs sit beside the counter directory as <dir>_*.log)
+    seen = set()
+    for logf in glob.glob(pmc_dir.rstrip("/") + "_*.log"):
+        for ln in open(logf, errors="replace"):
+            if ln.startswith("{") and "kernel_source_sha256_16" in ln:
+                seen.add(json.loads(ln)["kernel_source_sha256_16"])
+    if len(seen) > 1:
+        raise SystemExit(f"profiled runs disagree on the kernel source: {sorted(seen)}")
+    src_hash = seen.pop() if seen else kernel_source_hash()
+
     f_split, f_copy = per_kernel("FETCH_SIZE")
     w_split, w_copy = per_kernel("WRITE_SIZE")
     calib_kib = calib_mib * 1024.0
@@ -130,10 +141,21 @@ def pmc_summary(pmc_dir, workload, calib_mib, out_path):
     wf = calib_kib / max(w_copy)
     fetch = float(np.mean(f_split)) * rf * 1024
     write = float(np.mean(w_split)) * wf * 1024
+    rel = os.path.relpath(os.path.abspath(pmc_dir), ROOT)
+    run = (f"python -u $REPO/bench.py --steps 5 --warmup 2 --no-cpu --workload {workload} "
+           f"--calib-copy-mib {calib_mib}")
     lines = [
         f"# HBM traffic of mla_split_mfma, workload {workload}",
         "",
-        f"kernel_source_sha256_16: {kernel_source_hash()}",
+        "Commands (the two profiled runs from /tmp with TMPDIR=/tmp; REPO = repository root):",
+        "",
+        "```",
+        f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/{rel} -o pass3 -- {run}",
+        f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/{rel} -o pass4 -- {run}",
+        f"python bench.py --pmc-summary {rel} --workload {workload} --calib-copy-mib {calib_mib}",
+        "```",
+        "",
+        f"kernel_source_sha256_16: {src_hash}",
         f"dispatches: {len(f_split)} (FETCH_SIZE run), {len(w_split)} (WRITE_SIZE run)",
         f"FETCH_SIZE per dispatch (KiB, raw): {np.mean(f_split):.1f}",
         f"WRITE_SIZE per dispatch (KiB, raw): {np.mean(w_split):.1f}",
@@ -311,6 +333,7 @@ def main():
         "kv_gbs_unique": round(alg_path["kv_unique"] / (ms_per_step / 1e3) / 1e9, 2),
         "split_ms": round(split_avg, 5), "combine_ms": round(float(np.mean(comb_ms)), 5),
         "roofline": roof, "cpu_baseline": cpu,
+        "kernel_source_sha256_16": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
 
