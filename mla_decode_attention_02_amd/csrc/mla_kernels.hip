@@ -20,6 +20,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "mla_internal.h"
 
@@ -131,7 +132,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 //     (r & 15), 512 B each, with 16-byte chunk c at c ^ ((r >> 3) & 1)
 //   rope rows:   r * 128 B (bf16) or r * 64 B (fp8), 16-byte chunks XOR
 //     swizzled by row
-//   scales:      32 fp32 (fp8 only)
+//   scales:      32 fp32 (fp8 only), stored 8 times over so that one
+//     full-wave load fills them
 // These placements keep both LDS access patterns free of bank conflicts on a
 // 64-bank LDS -- the QK^T read (16 lanes = 16 rows, one logical 16-byte chunk)
 // and the transposed PV read (bf16: 4 rows x two 32-byte runs per 32 lanes;
@@ -145,7 +147,7 @@ struct Tile {
   static constexpr int kRope = FP8 ? 64 : 128;        // rope bytes per row
   static constexpr int kLatBytes = FP8 ? 16 * 1056 : 16 * 2176;
   static constexpr int kRopeBytes = 32 * kRope;
-  static constexpr int kScaleBytes = FP8 ? 128 : 0;
+  static constexpr int kScaleBytes = FP8 ? 1024 : 0;  // 8 copies of the 32 scales
   static constexpr int kStage = kLatBytes + kRopeBytes + kScaleBytes;
 
   static __device__ __forceinline__ int lat_base(int r) {
@@ -181,40 +183,36 @@ __device__ __forceinline__ uint32_t lds_addr(LDS_AS const void* p) {
   return (uint32_t)(uintptr_t)p;
 }
 
-// Issue the direct-to-LDS loads of one tile for this wave.  `tile_g` is the
-// first row of the tile in HBM (32 rows, contiguous within one page).
+// Direct-to-LDS load number q (0 <= q < loads_per_wave) of one tile for this
+// wave.  `tile_g` is the first row of the tile in HBM (32 rows, contiguous
+// within one page).
 template <bool FP8, int WAVES>
-__device__ __forceinline__ void issue_tile(const char* tile_g, const float* scale_g,
-                                           LDS_AS char* st, int wave, int lane) {
+__device__ __forceinline__ void issue_piece(const char* tile_g, const float* scale_g,
+                                            LDS_AS char* st, int wave, int lane, int q) {
   using G = Tile<FP8>;
   if constexpr (!FP8) {
-#pragma unroll
-    for (int q = 0; q < 32 / WAVES; ++q) {
+    if (q < 32 / WAVES) {  // latent rows
       const int r = wave + q * WAVES;
       const int c = lane ^ G::xlat(r);
       lds_dma16(tile_g, r * G::kRowBytes + 16 * c, lds_addr(st + G::lat_base(r)));
-    }
-#pragma unroll
-    for (int q = 0; q < 4 / WAVES; ++q) {
-      const int qq = wave + q * WAVES;
+    } else {  // rope: 8 rows per load
+      const int qq = wave + (q - 32 / WAVES) * WAVES;
       const int r = 8 * qq + (lane >> 3);
       const int c = (lane & 7) ^ G::xrope(r);
       lds_dma16(tile_g, r * G::kRowBytes + G::kLat + 16 * c,
                 lds_addr(st + G::kLatBytes + 1024 * qq));
     }
   } else {
-#pragma unroll
-    for (int q = 0; q < 16 / WAVES; ++q) {
-      const int pr = wave + q * WAVES;          // rows pr and pr + 16
+    if (q < 16 / WAVES) {  // latent rows pr and pr + 16
+      const int pr = wave + q * WAVES;
       const int r = pr + 16 * (lane >> 5);
       const int c = (lane & 31) ^ G::xlat(r);
       lds_dma16(tile_g, r * G::kRowBytes + 16 * c, lds_addr(st + pr * 1056));
-    }
-    // rope (2 instructions) and scales (1, lanes 0..7), spread so that every
-    // wave issues the same count; duplicate scale loads write the same bytes.
-    constexpr int kExtra = (WAVES == 4 ? 1 : (WAVES == 2 ? 2 : 3));
-#pragma unroll
-    for (int e = 0; e < kExtra; ++e) {
+    } else {
+      // rope (2 loads) and scales (1 load: lane l reads scale chunk l mod 8),
+      // spread so that every wave issues the same count; duplicate scale
+      // loads write the same bytes.
+      const int e = q - 16 / WAVES;
       int job;  // 0, 1 = rope halves; 2 = scales
       if (WAVES == 4) job = wave < 2 ? wave : 2;
       else if (WAVES == 2) job = e == 0 ? wave : 2;
@@ -224,11 +222,20 @@ __device__ __forceinline__ void issue_tile(const char* tile_g, const float* scal
         const int c = (lane & 3) ^ G::xrope(r);
         lds_dma16(tile_g, r * G::kRowBytes + G::kLat + 16 * c,
                   lds_addr(st + G::kLatBytes + 1024 * job));
-      } else if (lane < 8) {
-        lds_dma16(scale_g, 16 * lane, lds_addr(st + G::kLatBytes + G::kRopeBytes));
+      } else {
+        lds_dma16(scale_g, 16 * (lane & 7), lds_addr(st + G::kLatBytes + G::kRopeBytes));
       }
     }
   }
+}
+
+// All direct-to-LDS loads of one tile for this wave.
+template <bool FP8, int WAVES>
+__device__ __forceinline__ void issue_tile(const char* tile_g, const float* scale_g,
+                                           LDS_AS char* st, int wave, int lane) {
+#pragma unroll
+  for (int q = 0; q < Tile<FP8>::template loads_per_wave<WAVES>(); ++q)
+    issue_piece<FP8, WAVES>(tile_g, scale_g, st, wave, lane, q);
 }
 
 // Zero the rows r >= valid of a loaded tile (their slots are past the end of
@@ -271,8 +278,10 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
   switch (ahead) {
     case 0: wait_vmcnt<0>(); break;
     case 1: wait_vmcnt<N>(); break;
-    case 2: wait_vmcnt<2 * N < 64 ? 2 * N : 0>(); break;
-    default: wait_vmcnt<3 * N < 64 ? 3 * N : 0>(); break;
+    case 2: wait_vmcnt<(2 * N < 64 ? 2 * N : 0)>(); break;
+    case 3: wait_vmcnt<(3 * N < 64 ? 3 * N : 0)>(); break;
+    case 4: wait_vmcnt<(4 * N < 64 ? 4 * N : 0)>(); break;
+    default: wait_vmcnt<(5 * N < 64 ? 5 * N : 0)>(); break;
   }
 }
 
@@ -280,6 +289,22 @@ template <typename T>
 __device__ __forceinline__ T uniform_load(const T* p) {
   // wave-uniform address: read through the scalar cache
   return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// Score-tile MFMAs in inline assembly, with the accumulator constrained to
+// VGPRs.  The output accumulators take all 256 AGPRs; the compiler's builtin
+// would put this accumulator in AGPRs as well and shuffle output blocks out
+// of the way.  The compiler does not know these are MFMAs, so each one starts
+// with two wait states (enough for a VALU write of an operand just before),
+// and mfma_settle() waits out the result latency before the scores are read.
+__device__ __forceinline__ void mfma_v0(floatx16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(floatx16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_settle(floatx16& c) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(c));
 }
 
 // ------------------------------------------------------- MFMA split kernel
@@ -292,14 +317,20 @@ __device__ __forceinline__ T uniform_load(const T* p) {
 // operand read transposed from the same LDS tile (ds_read_b64_tr_b16 / _b8).
 // O^T for the wave's 32 rows x 512 latent columns is 16 accumulators (256
 // registers per lane).
+//
+// Software pipeline, per tile i: one barrier (tile i has landed, every wave
+// is done with tile i - 2, whose stage is refilled with tile i + STAGES - 2),
+// then the scores of tile i, then the value product of tile i - 1 with the
+// softmax of tile i interleaved between its MFMAs.
 template <bool FP8, int WAVES, int STAGES>
 __global__ void __launch_bounds__(64 * WAVES, 1)
 mla_split_mfma(SplitParams p, int groups) {
   using G = Tile<FP8>;
   constexpr int kRows = 32 * WAVES;
   constexpr int kLoads = G::template loads_per_wave<WAVES>();
-  static_assert((STAGES - 1) * kLoads < 64, "vmcnt range");
-  static_assert(STAGES >= 2 && STAGES <= 4, "stage count");
+  constexpr int kDepth = STAGES - 2;  // tiles loading ahead of the one being scored
+  static_assert(kDepth >= 1 && kDepth - 1 <= 5, "stage count");
+  static_assert((kDepth - 1) * kLoads < 64, "vmcnt range");
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)(LDS_AS void*)smem_raw;
 
@@ -366,53 +397,41 @@ mla_split_mfma(SplitParams p, int groups) {
   const int rho = swap_bits23(n);  // tile row feeding A-operand slot n
   const int64_t pt_row = (int64_t)b * p.MP;
 
+  auto stage_of = [&](int i) -> LDS_AS char* { return smem + (i % STAGES) * G::kStage; };
+  auto page_of = [&](int i) { return uniform_load(p.page_table + pt_row + (cb + 32 * i) / p.P); };
+  auto row_of = [&](int i, int page) { return (int64_t)page * p.P + ((cb + 32 * i) % p.P); };
   auto issue = [&](int i) {
-    const int ts = cb + 32 * i;
-    const int page = uniform_load(p.page_table + pt_row + ts / p.P);
-    const int64_t row0 = (int64_t)page * p.P + (ts % p.P);
+    const int64_t row0 = row_of(i, page_of(i));
     issue_tile<FP8, WAVES>(kv + row0 * G::kRowBytes, FP8 ? p.kv_scales + row0 : nullptr,
-                           smem + (i % STAGES) * G::kStage, wave, lane);
+                           stage_of(i), wave, lane);
   };
 
   // per-lane LDS read offsets (stage relative)
   const int k_off = G::lat_base(rho) + 16 * (FP8 ? (h ^ G::xlat(rho)) : 0);
   const int grp = lane >> 4, sl = lane & 15, dh = grp & 1;
 
-#pragma unroll
-  for (int i = 0; i < STAGES - 1; ++i)
-    if (i < ntiles) issue(i);
-
-  // Wait for tile i, refill the stage freed by tile i - 1, clear past-the-end
-  // rows; returns tile i's stage.
-  auto stage_in = [&](int i) -> LDS_AS char* {
-    const int ahead_tiles = ntiles - 1 - i;
-    wait_ahead<kLoads>(ahead_tiles < STAGES - 2 ? ahead_tiles : STAGES - 2);
-    __syncthreads();
-    if (i + STAGES - 1 < ntiles) issue(i + STAGES - 1);
-    LDS_AS char* st = smem + (i % STAGES) * G::kStage;
-    const int ts = cb + 32 * i;
-    if (ts + 32 > L) {  // last tile of the request: clear slots past its end
-      zero_tail_rows<FP8, WAVES>(st, L - ts, tid);
-      __syncthreads();
-    }
-    return st;
+  // S^T = K Q^T for one tile (32 tokens x 32 rows) in one accumulation chain
+  // (back-to-back dependent MFMAs still issue every 32 cycles), K operands
+  // read from LDS a few steps ahead of the MFMA using them.
+  // The loads of a later tile are issued a few at a time between the MFMAs,
+  // not in one burst that would stall on the vector-memory issue queue.
+  struct Loader {
+    const char* tg;
+    const float* sg;
+    LDS_AS char* dst;
   };
-
-  // S^T = K Q^T for one tile (32 tokens x 32 rows), then scaled (log2
-  // domain) and masked in place; returns the row maximum over the tile.
-  auto scores = [&](LDS_AS char* st, int ts, floatx16& sacc) -> float {
-    // Two independent accumulation chains (even / odd k-steps): a single
-    // dependent chain issues one MFMA per ~44 cycles instead of ~32.
+  auto scores = [&](LDS_AS char* st, floatx16& sacc, const Loader& ld, auto with_loads) {
+    constexpr bool kLd = decltype(with_loads)::value;
+    floatx16 s0;
+    const LDS_AS char* ropep = st + G::kLatBytes + rho * G::kRope;
+    const int swr = G::xrope(rho);
     if constexpr (!FP8) {
-      floatx16 s0 = floatx16{}, s1 = floatx16{};
       const LDS_AS char* rowp = st + k_off + 16 * h;
-      const LDS_AS char* ropep = st + G::kLatBytes + rho * G::kRope;
-      const int swr = G::xrope(rho);
       auto kaddr = [&](int kk) -> const LDS_AS bf16x8* {
         return kk < 32 ? (const LDS_AS bf16x8*)(rowp + 32 * kk)
                        : (const LDS_AS bf16x8*)(ropep + 16 * ((2 * (kk - 32) + h) ^ swr));
       };
-      constexpr int kAhead = 4;  // LDS reads in flight ahead of the MFMA using them
+      constexpr int kAhead = 4;
       bf16x8 ring[kAhead];
 #pragma unroll
       for (int kk = 0; kk < kAhead; ++kk) ring[kk] = *kaddr(kk);
@@ -420,167 +439,240 @@ mla_split_mfma(SplitParams p, int groups) {
       for (int kk = 0; kk < 36; ++kk) {
         const bf16x8 a = ring[kk % kAhead];
         if (kk + kAhead < 36) ring[kk % kAhead] = *kaddr(kk + kAhead);
-        if (kk & 1)
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s1, 0, 0, 0);
-        else
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s0, 0, 0, 0);
+        if (kLd && (kk & 3) == 2 && (kk >> 2) < kLoads)
+          issue_piece<FP8, WAVES>(ld.tg, ld.sg, ld.dst, wave, lane, kk >> 2);
+        if (kk == 0) mfma_v0(s0, a, qf[0]);
+        else mfma_v(s0, a, qf[kk]);
       }
-#pragma unroll
-      for (int kk = 0; kk < kAhead; ++kk) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-      for (int kk = 0; kk < 36 - kAhead; ++kk) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-#pragma unroll
-      for (int kk = 0; kk < kAhead; ++kk) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      sacc = s0 + s1;
     } else {
-      sacc = floatx16{};
       const LDS_AS char* rowp = st + k_off;
+      auto kaddr = [&](int kk) -> const LDS_AS uintx4* {
+        return kk < 16 ? (const LDS_AS uintx4*)(rowp + 32 * kk)
+                       : (const LDS_AS uintx4*)(ropep + 16 * ((2 * (kk - 16) + h) ^ swr));
+      };
+      constexpr int kAhead = 2;
+      uintx4 ring[kAhead];
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const uintx4 raw = *(const LDS_AS uintx4*)(rowp + 32 * kk);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16(raw[0], raw[1]),
-                                                        qf[2 * kk], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16(raw[2], raw[3]),
-                                                        qf[2 * kk + 1], sacc, 0, 0, 0);
-      }
-      const LDS_AS char* ropep = st + G::kLatBytes + rho * G::kRope;
-      const int swr = G::xrope(rho);
+      for (int kk = 0; kk < kAhead; ++kk) ring[kk] = *kaddr(kk);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uintx4 raw = *(const LDS_AS uintx4*)(ropep + 16 * ((2 * kk + h) ^ swr));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16(raw[0], raw[1]),
-                                                        qf[32 + 2 * kk], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16(raw[2], raw[3]),
-                                                        qf[33 + 2 * kk], sacc, 0, 0, 0);
+      for (int kk = 0; kk < 18; ++kk) {
+        const uintx4 raw = ring[kk % kAhead];
+        if (kk + kAhead < 18) ring[kk % kAhead] = *kaddr(kk + kAhead);
+        if (kLd && kk % 3 == 1 && kk / 3 < kLoads)
+          issue_piece<FP8, WAVES>(ld.tg, ld.sg, ld.dst, wave, lane, kk / 3);
+        const int q0 = kk < 16 ? 2 * kk : 32 + 2 * (kk - 16);
+        const bf16x8 a0 = e4m3x8_to_bf16(raw[0], raw[1]);
+        const bf16x8 a1 = e4m3x8_to_bf16(raw[2], raw[3]);
+        if (kk == 0) mfma_v0(s0, a0, qf[q0]);
+        else mfma_v(s0, a0, qf[q0]);
+        mfma_v(s0, a1, qf[q0 + 1]);
       }
     }
-    const LDS_AS float* tsc = (const LDS_AS float*)(st + G::kLatBytes + G::kRopeBytes);
-    const int lim_rel = lim - ts;
-    float mx = neg_inf();
-#pragma unroll
-    for (int i2 = 0; i2 < 16; ++i2) {
-      const int tok = 16 * (i2 >> 3) + 8 * h + (i2 & 7);
-      float v = sacc[i2];
-      if constexpr (FP8) v *= tsc[tok];
-      v *= scale_log2;
-      sacc[i2] = tok < lim_rel ? v : neg_inf();
-      mx = fmaxf(mx, sacc[i2]);
-    }
-    return half_swap_max(mx);
+    mfma_settle(s0);
+    sacc = s0;
   };
 
-  // p = 2^(z - m_ref) -> bf16 value-operand weights (FP8: times the row
-  // scale); O^T += V^T P^T with V^T read transposed from the latent tile.
-  auto accumulate = [&](LDS_AS char* st, const floatx16& z) {
-    const LDS_AS float* tsc = (const LDS_AS float*)(st + G::kLatBytes + G::kRopeBytes);
-    const float mu = m_ref == neg_inf() ? 0.0f : m_ref;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        // the normaliser sums the weights exactly as the PV product sees them
-        const __bf16 wb = (__bf16)fast_exp2(z[8 * q + j] - mu);
-        l_part += (float)wb;
-        if constexpr (FP8)
-          pb[q][j] = (__bf16)((float)wb * tsc[16 * q + 8 * h + j]);
-        else
-          pb[q][j] = wb;
-      }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if constexpr (!FP8) {
-        const int r0 = 16 * q + 8 * h + (sl >> 2);
-        const int r1 = r0 + 4;
-        const int cpart = 2 * dh + ((sl & 3) >> 1);
-        const LDS_AS char* b0p = st + G::lat_base(r0) + 16 * cpart + 8 * (sl & 1);
-        const LDS_AS char* b1p = st + G::lat_base(r1) + 16 * cpart + 8 * (sl & 1);
-        // whole-vector reinterpretation of the two transposed reads
-        // (element-wise bf16 inserts were miscompiled into a broadcast)
-        auto vread = [&](int db) -> bf16x8 {
-          const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(b0p + 64 * db));
-          const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(b1p + 64 * db));
-          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-        constexpr int kAhead = 3;  // value operands in flight ahead of their MFMA
-        bf16x8 ring[kAhead];
-#pragma unroll
-        for (int db = 0; db < kAhead; ++db) ring[db] = vread(db);
-#pragma unroll
-        for (int db = 0; db < 16; ++db) {
-          const bf16x8 a = ring[db % kAhead];
-          if (db + kAhead < 16) ring[db % kAhead] = vread(db + kAhead);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[q], acc[db], 0, 0, 0);
-        }
-#pragma unroll
-        for (int db = 0; db < kAhead; ++db) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int db = 0; db < 16 - kAhead; ++db) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-#pragma unroll
-        for (int db = 0; db < kAhead; ++db) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      } else {
-        const int r0 = 16 * q + 8 * h + (sl >> 1);
-        const LDS_AS char* bp = st + G::lat_base(r0) + 16 * (dh ^ G::xlat(r0)) + 8 * (sl & 1);
-#pragma unroll
-        for (int db = 0; db < 16; ++db) {
-          const intx2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS intx2*)(bp + 32 * db));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              e4m3x8_to_bf16((unsigned)v[0], (unsigned)v[1]), pb[q], acc[db], 0, 0, 0);
-        }
-      }
-    }
-  };
-
-  // Restart requests, one word per tile in a ring of three (after the
-  // pipeline stages): lanes write word i % 3 while handling tile i; every wave
-  // reads it after the barrier that opens tile i + 1 (so all waves see the
-  // same value and leave the loop together), and it is cleared after the
-  // barrier of tile i + 2, before tile i + 3 can write it again.
+  // Restart requests: word [i % 2][wave] is written by every wave while it
+  // handles tile i and read by all waves after the barrier that opens tile
+  // i + 1; it is next written for tile i + 2, after the following barrier.
   volatile LDS_AS int* req = (volatile LDS_AS int*)(smem + STAGES * G::kStage);
-  if (tid < 3) req[tid] = 0;  // ordered before any use by the first tile barrier
+  auto restart_asked = [&](int i) -> bool {
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) any |= req[(i & 1) * WAVES + w];
+    return __builtin_amdgcn_readfirstlane(any) != 0;
+  };
 
-  for (;;) {
+  // One step of the softmax of tile i (32 steps per tile, interleaved with the
+  // 32 MFMAs of the value product of tile i - 1).  Steps 0..15 scale (log2
+  // domain) and mask one score each and fold it into the row maximum; step
+  // 15 finishes the maximum across the lane pair, the reference maximum and
+  // the restart request; steps 16..31 turn one score each into a bf16 weight
+  // p = 2^(z - m_ref) (FP8: times the token's scale) and add the rounded
+  // weight to the normaliser; step 31 publishes this wave's restart request.
+  struct SoftmaxState {
+    float mx, mu;
+    bool over;
+  };
+  auto softmax_step = [&](int k, const float (&tscv)[16], int lim_rel, floatx16& z,
+                          bf16x8 (&pb)[2], SoftmaxState& sm, int i) {
+    if (k < 16) {
+      const int tok = 16 * (k >> 3) + 8 * h + (k & 7);
+      float v = z[k];
+      if constexpr (FP8) v *= tscv[k];
+      v *= scale_log2;
+      z[k] = tok < lim_rel ? v : neg_inf();
+      sm.mx = fmaxf(sm.mx, z[k]);
+      asm volatile("" : "+v"(sm.mx));  // keep this step's work in this step
+      if (k == 15) {
+        sm.mx = half_swap_max(sm.mx);
+        m_seen = fmaxf(m_seen, sm.mx);
+        m_ref = m_ref == neg_inf() ? sm.mx : m_ref;  // first tile with a visible token
+        sm.over = sm.mx > m_ref + kRestartMargin;
+        sm.mu = m_ref == neg_inf() ? 0.0f : m_ref;
+      }
+    } else {
+      const int e = k - 16, q = e >> 3, j = e & 7;
+      const __bf16 wb = (__bf16)fast_exp2(z[e] - sm.mu);
+      l_part += (float)wb;  // the normaliser sums the weights exactly as PV sees them
+      asm volatile("" : "+v"(l_part));  // keep this step's work in this step
+      if constexpr (FP8)
+        pb[q][j] = (__bf16)((float)wb * tscv[e]);
+      else
+        pb[q][j] = wb;
+      if (k == 31) req[(i & 1) * WAVES + wave] = __builtin_amdgcn_ballot_w64(sm.over) != 0 ? 1 : 0;
+    }
+  };
+
+  // O^T += V^T P^T for the tile in stage sv with weights pw, one softmax step
+  // of tile i after each MFMA (each step is its own scheduling region, so the
+  // VALU work sits between the MFMAs instead of after them).
+  auto values_softmax = [&](LDS_AS char* sv, const bf16x8 (&pw)[2], LDS_AS char* st, int i,
+                            floatx16& z, bf16x8 (&pb)[2]) {
+    const int lim_rel = lim - (cb + 32 * i);
+    SoftmaxState sm{neg_inf(), 0.0f, false};
+    // FP8: the scales of this lane's 16 tokens (two runs of 8), read up front
+    // so that no step waits on an LDS read behind the value prefetches
+    float tscv[16];
+    if constexpr (FP8) {
+      const LDS_AS float* tsc = (const LDS_AS float*)(st + G::kLatBytes + G::kRopeBytes);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const floatx4 u0 = *(const LDS_AS floatx4*)(tsc + 16 * r + 8 * h);
+        const floatx4 u1 = *(const LDS_AS floatx4*)(tsc + 16 * r + 8 * h + 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          tscv[8 * r + c] = u0[c];
+          tscv[8 * r + 4 + c] = u1[c];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) tscv[c] = 1.0f;
+    }
+    if constexpr (!FP8) {
+      const LDS_AS char* bp[2][2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int r0 = 16 * q + 8 * h + (sl >> 2);
+        const int cpart = 2 * dh + ((sl & 3) >> 1);
+        bp[q][0] = sv + G::lat_base(r0) + 16 * cpart + 8 * (sl & 1);
+        bp[q][1] = sv + G::lat_base(r0 + 4) + 16 * cpart + 8 * (sl & 1);
+      }
+      // whole-vector reinterpretation of the two transposed reads
+      // (element-wise bf16 inserts were miscompiled into a broadcast)
+      auto vread = [&](int x2) -> bf16x8 {
+        const int q = x2 >> 4, db = x2 & 15;
+        const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(bp[q][0] + 64 * db));
+        const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(bp[q][1] + 64 * db));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      constexpr int kAhead = 3;  // value operands in flight ahead of their MFMA
+      bf16x8 ring[kAhead];
+#pragma unroll
+      for (int x2 = 0; x2 < kAhead; ++x2) ring[x2] = vread(x2);
+#pragma unroll
+      for (int x2 = 0; x2 < 32; ++x2) {
+        const bf16x8 a = ring[x2 % kAhead];
+        if (x2 + kAhead < 32) ring[x2 % kAhead] = vread(x2 + kAhead);
+        acc[x2 & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pw[x2 >> 4], acc[x2 & 15], 0, 0, 0);
+        softmax_step(x2, tscv, lim_rel, z, pb, sm, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      const LDS_AS char* bp[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int r0 = 16 * q + 8 * h + (sl >> 1);
+        bp[q] = sv + G::lat_base(r0) + 16 * (dh ^ G::xlat(r0)) + 8 * (sl & 1);
+      }
+      auto vread = [&](int x2) -> intx2 {
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS intx2*)(bp[x2 >> 4] + 32 * (x2 & 15)));
+      };
+      constexpr int kAhead = 3;
+      intx2 ring[kAhead];
+#pragma unroll
+      for (int x2 = 0; x2 < kAhead; ++x2) ring[x2] = vread(x2);
+#pragma unroll
+      for (int x2 = 0; x2 < 32; ++x2) {
+        const intx2 v = ring[x2 % kAhead];
+        if (x2 + kAhead < 32) ring[x2 % kAhead] = vread(x2 + kAhead);
+        acc[x2 & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            e4m3x8_to_bf16((unsigned)v[0], (unsigned)v[1]), pw[x2 >> 4], acc[x2 & 15], 0, 0, 0);
+        softmax_step(x2, tscv, lim_rel, z, pb, sm, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // The value product "of tile -1" in the first step reads the last stage with
+  // zero weights: clear it so that it holds no NaN.
+  auto clear_stage = [&](LDS_AS char* st) {
+    for (int o = 16 * tid; o < G::kStage; o += 16 * 64 * WAVES)
+      *(LDS_AS uintx4*)(st + o) = uintx4{0, 0, 0, 0};
+  };
+  clear_stage(stage_of(STAGES - 1));
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i)
+    if (i < ntiles) issue(i);
+
+  bf16x8 pprev[2] = {bf16x8{}, bf16x8{}};
+  // page of the next tile to load, read one step ahead of its use
+  int pg_next = kDepth < ntiles ? page_of(kDepth) : 0;
+  for (; ntiles > 0;) {
     bool restart = false;
-    int w_cur = 0, w_prev = 2, w_old = 1;  // i % 3, (i - 1) % 3, (i - 2) % 3
-    for (int i = 0; i < ntiles; ++i) {
-      LDS_AS char* st = stage_in(i);
-      if (i >= 1 && req[w_prev]) {
+    // Step i scores tile i (if i < ntiles) and accumulates the values of
+    // tile i - 1; step ntiles only finishes the last tile.
+    for (int i = 0; i <= ntiles; ++i) {
+      const int ahead_tiles = ntiles - 1 - i;
+      wait_ahead<kLoads>(ahead_tiles < 0 ? 0 : (ahead_tiles < kDepth - 1 ? ahead_tiles : kDepth - 1));
+      __syncthreads();
+      if (i >= 1 && restart_asked(i - 1)) {
         restart = true;
         break;
       }
-      if (i >= 2 && tid == 0) req[w_old] = 0;
+      // tile i + kDepth goes to the stage freed by tile i - 2
+      const int64_t row0 = row_of(i + kDepth, pg_next);
+      const Loader ld{kv + row0 * G::kRowBytes, FP8 ? p.kv_scales + row0 : nullptr,
+                      stage_of(i + kDepth)};
+      LDS_AS char* st = stage_of(i);
+      const int ts = cb + 32 * i;
+      if (i < ntiles && ts + 32 > L) {  // last tile of the request: clear slots past its end
+        zero_tail_rows<FP8, WAVES>(st, L - ts, tid);
+        __syncthreads();
+      }
+      // step ntiles scores whatever its stage holds: every token is masked.
+      // One uniform branch per step picks the variant with or without loads,
+      // so that the MFMA loop itself has no branches.
       floatx16 z;
-      const float mx = scores(st, cb + 32 * i, z);
-      m_seen = fmaxf(m_seen, mx);
-      if (m_ref == neg_inf()) m_ref = mx;  // first visible tile of this row
-      if (mx > m_ref + kRestartMargin) req[w_cur] = 1;
-      accumulate(st, z);
-      w_old = w_prev;
-      w_prev = w_cur;
-      w_cur = w_cur == 2 ? 0 : w_cur + 1;
-    }
-    if (!restart && ntiles > 0) {  // the last tile may have asked for a restart too
-      __syncthreads();
-      restart = req[w_prev] != 0;
+      if (i + kDepth < ntiles)
+        scores(st, z, ld, std::true_type{});
+      else
+        scores(st, z, ld, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 pcur[2];
+      values_softmax(stage_of(i + STAGES - 1), pprev, st, i, z, pcur);
+      pprev[0] = pcur[0];
+      pprev[1] = pcur[1];
+      // branch-free: past the last tile this re-reads a valid entry and is unused
+      pg_next = uniform_load(p.page_table + pt_row +
+                             (i + kDepth + 1 < ntiles ? (cb + 32 * (i + kDepth + 1)) / p.P : 0));
     }
     if (!restart) break;
     // Rare path: drain the pipeline, reset, and run the chunk again.
     wait_vmcnt<0>();
     __syncthreads();
-    if (tid < 3) req[tid] = 0;
+    clear_stage(stage_of(STAGES - 1));
     m_ref = m_seen;
     l_part = 0.0f;
+    pprev[0] = bf16x8{};
+    pprev[1] = bf16x8{};
 #pragma unroll
     for (int db = 0; db < 16; ++db) acc[db] = floatx16{};
 #pragma unroll
-    for (int i = 0; i < STAGES - 1; ++i)
+    for (int i = 0; i < kDepth; ++i)
       if (i < ntiles) issue(i);
+    pg_next = kDepth < ntiles ? page_of(kDepth) : 0;
   }
 
   // ---- epilogue: normalise and write (lane pair n, n+32 shares row gr)
@@ -794,7 +886,7 @@ hipError_t launch_mfma(const SplitParams& p, hipStream_t stream) {
   const int groups = (M + kRows - 1) / kRows;
   const int units = p.B * p.S;
   const int64_t blocks = 8LL * groups * ((units + 7) / 8);
-  const size_t lds = (size_t)STAGES * Tile<FP8>::kStage + 16;  // + restart request ring
+  const size_t lds = (size_t)STAGES * Tile<FP8>::kStage + 8 * WAVES;  // + restart requests
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
@@ -821,7 +913,7 @@ Kernel pick_kernel(const SplitParams& p) {
 hipError_t launch_split(const SplitParams& p, hipStream_t stream) {
   switch (pick_kernel(p)) {
     case Kernel::kMfmaBf16: return launch_mfma<false, 4, 4>(p, stream);
-    case Kernel::kMfmaFp8: return launch_mfma<true, 4, 4>(p, stream);
+    case Kernel::kMfmaFp8: return launch_mfma<true, 4, 8>(p, stream);
     default: break;
   }
   const int M = p.T * p.H;
