@@ -388,11 +388,13 @@ mla_split_mfma(SplitParams p, int groups) {
   // (zeroing the accumulators), which real attention logits never trigger.
   float m_ref = neg_inf();
   float m_seen = neg_inf();  // largest tile maximum seen so far
-  float l_part = 0.0f;       // this lane-half's share of the normaliser
+  float l_part = 0.0f;       // this lane-half's share of the normaliser (odd
+  float l_part2 = 0.0f;      // and even scores in two sums)
   const float scale_log2 = p.scale * kLog2e;
   constexpr float kRestartMargin = 60.0f;
 
   const int ntiles = (ce - cb + 31) >> 5;
+
   const char* kv = (const char*)p.kv;
   const int rho = swap_bits23(n);  // tile row feeding A-operand slot n
   const int64_t pt_row = (int64_t)b * p.MP;
@@ -476,51 +478,79 @@ mla_split_mfma(SplitParams p, int groups) {
   // handles tile i and read by all waves after the barrier that opens tile
   // i + 1; it is next written for tile i + 2, after the following barrier.
   volatile LDS_AS int* req = (volatile LDS_AS int*)(smem + STAGES * G::kStage);
-  auto restart_asked = [&](int i) -> bool {
+  auto restart_word = [&](int i) -> int {
     int any = 0;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) any |= req[(i & 1) * WAVES + w];
-    return __builtin_amdgcn_readfirstlane(any) != 0;
+    return any;
   };
 
   // One step of the softmax of tile i (32 steps per tile, interleaved with the
-  // 32 MFMAs of the value product of tile i - 1).  Steps 0..15 scale (log2
-  // domain) and mask one score each and fold it into the row maximum; step
-  // 15 finishes the maximum across the lane pair, the reference maximum and
-  // the restart request; steps 16..31 turn one score each into a bf16 weight
-  // p = 2^(z - m_ref) (FP8: times the token's scale) and add the rounded
-  // weight to the normaliser; step 31 publishes this wave's restart request.
+  // 32 MFMAs of the value product of tile i - 1); each step works on two
+  // scores so that its instructions form two independent chains:
+  //   steps 0..7    mask scores 2k, 2k+1 (FP8: times the token scale) and
+  //                 fold them into two running maxima;
+  //   step 8        the row maximum across both halves and the lane pair,
+  //                 times s = scale * log2 e (s > 0: max(s z) = s max(z)
+  //                 exactly, rounding being monotonic);
+  //   step 9        the reference maximum and the restart request;
+  //   steps 10..17  p = 2^(s z - m_ref) for scores 2(k-10), 2(k-10)+1;
+  //   steps 18..25  round two weights to bf16 for the value product (FP8:
+  //                 times the token scale) and add the rounded weights to the
+  //                 normaliser, exactly as the product sees them;
+  //   step 26       publish this wave's restart request.
   struct SoftmaxState {
-    float mx, mu;
+    float mx_a, mx_b, mu;
     bool over;
   };
+  // running maximum without the NaN canonicalisation fmaxf implies; the
+  // volatile statement also keeps the step's work in its step
+  auto vmax = [](float& m, float x) { asm volatile("v_max_f32 %0, %0, %1" : "+v"(m) : "v"(x)); };
   auto softmax_step = [&](int k, const float (&tscv)[16], int lim_rel, floatx16& z,
                           bf16x8 (&pb)[2], SoftmaxState& sm, int i) {
-    if (k < 16) {
-      const int tok = 16 * (k >> 3) + 8 * h + (k & 7);
-      float v = z[k];
-      if constexpr (FP8) v *= tscv[k];
-      v *= scale_log2;
-      z[k] = tok < lim_rel ? v : neg_inf();
-      sm.mx = fmaxf(sm.mx, z[k]);
-      asm volatile("" : "+v"(sm.mx));  // keep this step's work in this step
-      if (k == 15) {
-        sm.mx = half_swap_max(sm.mx);
-        m_seen = fmaxf(m_seen, sm.mx);
-        m_ref = m_ref == neg_inf() ? sm.mx : m_ref;  // first tile with a visible token
-        sm.over = sm.mx > m_ref + kRestartMargin;
-        sm.mu = m_ref == neg_inf() ? 0.0f : m_ref;
+    if (k < 8) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = 2 * k + u;
+        const int tok = 16 * (e >> 3) + 8 * h + (e & 7);
+        float v = z[e];
+        if constexpr (FP8) v *= tscv[e];
+        z[e] = tok < lim_rel ? v : neg_inf();
       }
-    } else {
-      const int e = k - 16, q = e >> 3, j = e & 7;
-      const __bf16 wb = (__bf16)fast_exp2(z[e] - sm.mu);
-      l_part += (float)wb;  // the normaliser sums the weights exactly as PV sees them
-      asm volatile("" : "+v"(l_part));  // keep this step's work in this step
-      if constexpr (FP8)
-        pb[q][j] = (__bf16)((float)wb * tscv[e]);
-      else
-        pb[q][j] = wb;
-      if (k == 31) req[(i & 1) * WAVES + wave] = __builtin_amdgcn_ballot_w64(sm.over) != 0 ? 1 : 0;
+      vmax(sm.mx_a, z[2 * k]);
+      vmax(sm.mx_b, z[2 * k + 1]);
+    } else if (k == 8) {
+      float mx = sm.mx_a;
+      vmax(mx, sm.mx_b);
+      sm.mx_a = half_swap_max(mx) * scale_log2;
+      asm volatile("" : "+v"(sm.mx_a));
+    } else if (k == 9) {
+      const float mx = sm.mx_a;
+      m_seen = fmaxf(m_seen, mx);
+      m_ref = m_ref == neg_inf() ? mx : m_ref;  // first tile with a visible token
+      sm.over = mx > m_ref + kRestartMargin;
+      sm.mu = m_ref == neg_inf() ? 0.0f : m_ref;
+      asm volatile("" : "+v"(sm.mu));
+    } else if (k < 18) {
+      const int e = 2 * (k - 10);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) z[e + u] = fast_exp2(__builtin_fmaf(z[e + u], scale_log2, -sm.mu));
+      asm volatile("" : "+v"(z));
+    } else if (k < 26) {
+      const int e = 2 * (k - 18), q = e >> 3, j = e & 7;
+      const __bf16 w0 = (__bf16)z[e], w1 = (__bf16)z[e + 1];
+      l_part += (float)w0;  // the normaliser sums the weights exactly as PV sees them
+      l_part2 += (float)w1;
+      if constexpr (FP8) {
+        pb[q][j] = (__bf16)((float)w0 * tscv[e]);
+        pb[q][j + 1] = (__bf16)((float)w1 * tscv[e + 1]);
+      } else {
+        pb[q][j] = w0;
+        pb[q][j + 1] = w1;
+      }
+      asm volatile("" : "+v"(l_part), "+v"(l_part2));
+    } else if (k == 26) {
+      req[(i & 1) * WAVES + wave] = __builtin_amdgcn_ballot_w64(sm.over) != 0 ? 1 : 0;
     }
   };
 
@@ -530,7 +560,7 @@ mla_split_mfma(SplitParams p, int groups) {
   auto values_softmax = [&](LDS_AS char* sv, const bf16x8 (&pw)[2], LDS_AS char* st, int i,
                             floatx16& z, bf16x8 (&pb)[2]) {
     const int lim_rel = lim - (cb + 32 * i);
-    SoftmaxState sm{neg_inf(), 0.0f, false};
+    SoftmaxState sm{neg_inf(), neg_inf(), 0.0f, false};
     // FP8: the scales of this lane's 16 tokens (two runs of 8), read up front
     // so that no step waits on an LDS read behind the value prefetches
     float tscv[16];
@@ -627,10 +657,8 @@ mla_split_mfma(SplitParams p, int groups) {
       const int ahead_tiles = ntiles - 1 - i;
       wait_ahead<kLoads>(ahead_tiles < 0 ? 0 : (ahead_tiles < kDepth - 1 ? ahead_tiles : kDepth - 1));
       __syncthreads();
-      if (i >= 1 && restart_asked(i - 1)) {
-        restart = true;
-        break;
-      }
+      // restart requests of tile i - 1: read now, acted on after the scores
+      const int asked = i >= 1 ? restart_word(i - 1) : 0;
       // tile i + kDepth goes to the stage freed by tile i - 2
       const int64_t row0 = row_of(i + kDepth, pg_next);
       const Loader ld{kv + row0 * G::kRowBytes, FP8 ? p.kv_scales + row0 : nullptr,
@@ -649,6 +677,10 @@ mla_split_mfma(SplitParams p, int groups) {
         scores(st, z, ld, std::true_type{});
       else
         scores(st, z, ld, std::false_type{});
+      if (__builtin_amdgcn_readfirstlane(asked) != 0) {
+        restart = true;
+        break;
+      }
       __builtin_amdgcn_sched_barrier(0);
       bf16x8 pcur[2];
       values_softmax(stage_of(i + STAGES - 1), pprev, st, i, z, pcur);
@@ -665,6 +697,7 @@ mla_split_mfma(SplitParams p, int groups) {
     clear_stage(stage_of(STAGES - 1));
     m_ref = m_seen;
     l_part = 0.0f;
+    l_part2 = 0.0f;
     pprev[0] = bf16x8{};
     pprev[1] = bf16x8{};
 #pragma unroll
@@ -676,7 +709,7 @@ mla_split_mfma(SplitParams p, int groups) {
   }
 
   // ---- epilogue: normalise and write (lane pair n, n+32 shares row gr)
-  const float l_tot = half_swap_sum(l_part);
+  const float l_tot = half_swap_sum(l_part + l_part2);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_v = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : neg_inf();
   if (!row_ok) return;
@@ -904,8 +937,10 @@ hipError_t launch_mfma(const SplitParams& p, hipStream_t stream) {
 
 Kernel pick_kernel(const SplitParams& p) {
   if (p.force_generic) return Kernel::kGeneric;
+  // the MFMA kernel folds the scale into its exponent and takes the row
+  // maximum before scaling, which needs scale > 0
   const bool mfma_shape = p.Dc == 512 && p.Dr == 64 && p.q_dtype == kBF16 && p.P % 32 == 0 &&
-                          (p.kv_dtype == kBF16 || p.kv_dtype == kFP8);
+                          (p.kv_dtype == kBF16 || p.kv_dtype == kFP8) && p.scale > 0.0f;
   if (!mfma_shape) return Kernel::kGeneric;
   return p.kv_dtype == kFP8 ? Kernel::kMfmaFp8 : Kernel::kMfmaBf16;
 }
