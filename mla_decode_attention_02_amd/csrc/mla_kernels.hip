@@ -170,13 +170,15 @@ struct Tile {
 // Issued through inline assembly so that the compiler does not guard every
 // later LDS read with a wait for all outstanding loads; the kernel orders
 // them itself with s_waitcnt vmcnt + a workgroup barrier before a stage is
-// read, and a barrier before a stage is refilled.
+// read, and a barrier before a stage is refilled.  The load takes its LDS
+// address from M0, and a scalar write of M0 needs one wait state before a
+// direct-to-LDS load reads it.
 __device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff, uint32_t lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform by construction
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(gbase), "s"(m0v)
-               : "memory");
+               : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(LDS_AS const void* p) {
@@ -294,17 +296,28 @@ __device__ __forceinline__ T uniform_load(const T* p) {
 // Score-tile MFMAs in inline assembly, with the accumulator constrained to
 // VGPRs.  The output accumulators take all 256 AGPRs; the compiler's builtin
 // would put this accumulator in AGPRs as well and shuffle output blocks out
-// of the way.  The compiler does not know these are MFMAs, so each one starts
-// with two wait states (enough for a VALU write of an operand just before),
-// and mfma_settle() waits out the result latency before the scores are read.
+// of the way.  The compiler does not know these are MFMAs, so it models none
+// of their hazards, and the helpers cover them:
+//   - each MFMA starts with two wait states (enough for a VALU write of an
+//     operand just before);
+//   - the chain accumulates in place, so the only writer of the accumulator
+//     while an MFMA may still read it is the next MFMA of the same chain;
+//   - the last MFMA waits out its result latency inside the same statement,
+//     so no instruction the compiler places after it (a copy of the
+//     accumulator included) can read the result early.
+// A and B are read when an MFMA issues; only the accumulator is read later.
 __device__ __forceinline__ void mfma_v0(floatx16& c, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_v(floatx16& c, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma_settle(floatx16& c) {
-  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(c));
+__device__ __forceinline__ void mfma_v_last(floatx16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile(
+      "s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : "+v"(c)
+      : "v"(a), "v"(b));
 }
 
 // ------------------------------------------------------- MFMA split kernel
@@ -444,7 +457,8 @@ mla_split_mfma(SplitParams p, int groups) {
         if (kLd && (kk & 3) == 2 && (kk >> 2) < kLoads)
           issue_piece<FP8, WAVES>(ld.tg, ld.sg, ld.dst, wave, lane, kk >> 2);
         if (kk == 0) mfma_v0(s0, a, qf[0]);
-        else mfma_v(s0, a, qf[kk]);
+        else if (kk < 35) mfma_v(s0, a, qf[kk]);
+        else mfma_v_last(s0, a, qf[kk]);
       }
     } else {
       const LDS_AS char* rowp = st + k_off;
@@ -467,10 +481,10 @@ mla_split_mfma(SplitParams p, int groups) {
         const bf16x8 a1 = e4m3x8_to_bf16(raw[2], raw[3]);
         if (kk == 0) mfma_v0(s0, a0, qf[q0]);
         else mfma_v(s0, a0, qf[q0]);
-        mfma_v(s0, a1, qf[q0 + 1]);
+        if (kk < 17) mfma_v(s0, a1, qf[q0 + 1]);
+        else mfma_v_last(s0, a1, qf[q0 + 1]);
       }
     }
-    mfma_settle(s0);
     sacc = s0;
   };
 
