@@ -22,7 +22,11 @@ MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE = -1, -2, -3
 MLA_ERR_HIP, MLA_ERR_CHECK = -4, -5
 
 EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_decode_split",
-           "mla_combine", "mla_gather_rows", "mla_check_tables", "mla_status_string")
+           "mla_combine", "mla_balanced_workgroups", "mla_plan_balanced",
+           "mla_decode_split_balanced", "mla_combine_balanced", "mla_gather_rows",
+           "mla_check_tables", "mla_status_string")
+
+BALANCED_ROWS = 128  # rows per unit of the balanced work list
 
 
 class MLAError(RuntimeError):
@@ -58,6 +62,11 @@ def library():
     lib.mla_decode.argtypes = [PP, P, P, P, P, P, P, ctypes.c_float, P, P, P, sz, P]
     lib.mla_decode_split.argtypes = [PP, P, P, P, P, P, P, ctypes.c_float, i32, P, P, P]
     lib.mla_combine.argtypes = [i32, i32, i32, i32, P, P, i32, P, P, P]
+    lib.mla_balanced_workgroups.argtypes = [ctypes.POINTER(i32)]
+    lib.mla_plan_balanced.argtypes = [PP, P, P, P]
+    lib.mla_decode_split_balanced.argtypes = [PP, P, P, P, P, P, P, ctypes.c_float, i32, P, P, P,
+                                              P, P, P]
+    lib.mla_combine_balanced.argtypes = [PP, i32, P, P, P, P, P, P]
     lib.mla_gather_rows.argtypes = [PP, P, P, i32, P, P, P, P]
     lib.mla_check_tables.argtypes = [PP, P, P]
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -206,6 +215,65 @@ def decode_split(q_abs, q_rope, kv_pages, page_table, seq_lens, scale, num_split
                                       _ptr(partial_o), _ptr(partial_lse), _stream()),
            "mla_decode_split")
     return partial_o, partial_lse
+
+
+def balanced_workgroups():
+    """Workgroups of the balanced work list on the current device."""
+    n = ctypes.c_int32(0)
+    _check(library().mla_balanced_workgroups(ctypes.byref(n)), "mla_balanced_workgroups")
+    return int(n.value)
+
+
+def plan_balanced(problem, seq_lens, tile_prefix=None):
+    """Balanced plan: tile_prefix [U + 1] int32 (exclusive prefix of tiles per unit)."""
+    dev = seq_lens.device
+    _require(seq_lens, "seq_lens", dev, dtype=torch.int32, ndim=1)
+    groups = -(-problem.q_len * problem.num_heads // BALANCED_ROWS)
+    n = problem.batch * groups + 1
+    if tile_prefix is None:
+        tile_prefix = torch.empty(n, dtype=torch.int32, device=dev)
+    _require(tile_prefix, "tile_prefix", dev, dtype=torch.int32)
+    if tile_prefix.numel() < n:
+        raise ValueError("tile_prefix too small")
+    _check(library().mla_plan_balanced(ctypes.byref(problem), _ptr(seq_lens), _ptr(tile_prefix),
+                                       _stream()), "mla_plan_balanced")
+    return tile_prefix
+
+
+def decode_split_balanced(problem, q_abs, q_rope, kv_pages, page_table, seq_lens, scale,
+                          num_workgroups, tile_prefix, out, lse, slot_o, slot_lse, *,
+                          kv_scales=None):
+    """Split stage of the balanced work list (writes whole units to out/lse, other
+    segments to slot_o [2 nw, 128, Dc] / slot_lse [2 nw, 128])."""
+    _validate(q_abs, q_rope, kv_pages, page_table, seq_lens, kv_scales)
+    dev = q_abs.device
+    nw = int(num_workgroups)
+    _require(tile_prefix, "tile_prefix", dev, dtype=torch.int32)
+    _require(out, "out", dev, dtype=_torch_dtype(problem.out_dtype))
+    _require(lse, "lse", dev, dtype=torch.float32)
+    _require(slot_o, "slot_o", dev, dtype=torch.float32)
+    _require(slot_lse, "slot_lse", dev, dtype=torch.float32)
+    if (slot_o.numel() < 2 * nw * BALANCED_ROWS * problem.d_latent
+            or slot_lse.numel() < 2 * nw * BALANCED_ROWS):
+        raise ValueError("slot buffers too small")
+    _check(library().mla_decode_split_balanced(
+        ctypes.byref(problem), _ptr(q_abs), _ptr(q_rope), _ptr(kv_pages), _ptr(kv_scales),
+        _ptr(page_table), _ptr(seq_lens), ctypes.c_float(float(scale)), nw, _ptr(tile_prefix),
+        _ptr(out), _ptr(lse), _ptr(slot_o), _ptr(slot_lse), _stream()),
+        "mla_decode_split_balanced")
+
+
+def combine_balanced(problem, num_workgroups, tile_prefix, slot_o, slot_lse, out, lse):
+    """Merge stage of the balanced work list into out/lse."""
+    dev = out.device
+    for t, name in ((tile_prefix, "tile_prefix"), (slot_o, "slot_o"), (slot_lse, "slot_lse"),
+                    (lse, "lse")):
+        _require(t, name, dev)
+    _require(out, "out", dev, dtype=_torch_dtype(problem.out_dtype))
+    _check(library().mla_combine_balanced(ctypes.byref(problem), int(num_workgroups),
+                                          _ptr(tile_prefix), _ptr(slot_o), _ptr(slot_lse),
+                                          _ptr(out), _ptr(lse), _stream()),
+           "mla_combine_balanced")
 
 
 def combine(partial_o, partial_lse, *, out_dtype=torch.bfloat16, out=None, lse=None):

@@ -34,6 +34,12 @@ bool env_force_generic() {
   return v && v[0] == 'g';
 }
 
+// MLA_PLAN=uniform turns the balanced work list off (comparisons, tests).
+bool env_force_uniform() {
+  const char* v = getenv("MLA_PLAN");
+  return v && v[0] == 'u';
+}
+
 bool valid_dtype(int32_t d) { return d == MLA_DTYPE_F32 || d == MLA_DTYPE_BF16 || d == MLA_DTYPE_FP8_E4M3; }
 
 int validate_problem(const mla_problem* pr) {
@@ -79,6 +85,60 @@ size_t partial_bytes(const mla_problem* pr, int32_t S) {
   const size_t o = rows * pr->d_latent * sizeof(float);
   const size_t o_aligned = (o + 255) & ~(size_t)255;
   return o_aligned + rows * sizeof(float);
+}
+
+// The balanced work list's tile indices are int32: all tiles of all units
+// must fit.
+bool balanced_size_ok(const mla_problem* pr) {
+  const int64_t units = mla::balanced_units(pr->batch, pr->q_len, pr->num_heads);
+  const int64_t max_tiles = ((int64_t)pr->max_pages_per_seq * pr->page_size + 31) / 32;
+  return units < (int64_t)INT32_MAX / 2 && units * max_tiles < (int64_t)INT32_MAX / 2;
+}
+
+// Balanced work list (used by mla_decode when the library chooses the plan,
+// the uniform plan would split, and the MFMA kernels serve the shape): one
+// workgroup per compute unit, partial slots [NB][2][kBalancedRows].
+bool balanced_shape(const mla_problem* pr) {
+  if (pr->num_splits != 0 || plan_splits(pr) <= 1) return false;
+  if (!(pr->d_latent == 512 && pr->d_rope == 64 && pr->q_dtype == MLA_DTYPE_BF16 &&
+        pr->page_size % 32 == 0 &&
+        (pr->kv_dtype == MLA_DTYPE_BF16 || pr->kv_dtype == MLA_DTYPE_FP8_E4M3)))
+    return false;
+  return balanced_size_ok(pr);
+}
+
+int32_t device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cus;
+}
+
+struct BalancedLayout {
+  size_t prefix_off, lse_off, o_off, total;
+};
+
+BalancedLayout balanced_layout(const mla_problem* pr, int32_t NB) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t units = (size_t)mla::balanced_units(pr->batch, pr->q_len, pr->num_heads);
+  const size_t slot_rows = (size_t)NB * 2 * mla::kBalancedRows;
+  BalancedLayout l;
+  l.prefix_off = 0;
+  l.lse_off = up((units + 1) * sizeof(int32_t));
+  l.o_off = l.lse_off + up(slot_rows * sizeof(float));
+  l.total = l.o_off + slot_rows * (size_t)pr->d_latent * sizeof(float);
+  return l;
+}
+
+// Workspace for everything mla_decode may run: the uniform plan's partials
+// and, where it may apply, the balanced work list's.
+size_t decode_workspace(const mla_problem* pr, int32_t S, int32_t NB) {
+  size_t need = S > 1 ? partial_bytes(pr, S) : 0;
+  if (NB > 0 && balanced_shape(pr)) {
+    const size_t bal = balanced_layout(pr, NB).total;
+    if (bal > need) need = bal;
+  }
+  return need;
 }
 
 SplitParams make_params(const mla_problem* pr, const void* q_abs, const void* q_rope, const void* kv,
@@ -146,7 +206,7 @@ int mla_workspace_size(const mla_problem* problem, size_t* bytes) {
   if (rc) return rc;
   if (!bytes) return MLA_ERR_INVALID_ARG;
   const int32_t S = plan_splits(problem);
-  *bytes = S > 1 ? partial_bytes(problem, S) : 0;
+  *bytes = decode_workspace(problem, S, balanced_shape(problem) ? device_cus() : 0);
   return MLA_OK;
 }
 
@@ -200,13 +260,35 @@ int mla_decode(const mla_problem* problem, const void* q_absorbed, const void* q
   if (problem->batch == 0) return MLA_OK;
   if (!out) return MLA_ERR_INVALID_ARG;
   const int32_t S = plan_splits(problem);
-  const size_t need = S > 1 ? partial_bytes(problem, S) : 0;
+  const int32_t NB = balanced_shape(problem) && !env_force_uniform() ? device_cus() : 0;
+  const size_t need = decode_workspace(problem, S, NB);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
     return MLA_ERR_WORKSPACE;
   rc = run_checked_mode(problem, page_table, seq_lens, stream);
   if (rc) return rc;
   SplitParams p = make_params(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table,
                               seq_lens, scale, S);
+  if (NB > 0 && mla::pick_kernel(p) != mla::Kernel::kGeneric) {
+    // the stages of mla_plan_balanced, mla_decode_split_balanced and
+    // mla_combine_balanced, arguments already validated
+    const BalancedLayout l = balanced_layout(problem, NB);
+    const int32_t M = problem->q_len * problem->num_heads;
+    const int32_t groups = (M + mla::kBalancedRows - 1) / mla::kBalancedRows;
+    int32_t* prefix = (int32_t*)((char*)workspace + l.prefix_off);
+    p.NB = NB;
+    p.tile_prefix = prefix;
+    p.write_final = false;
+    p.out = out;
+    p.lse = lse;
+    p.part_lse = (float*)((char*)workspace + l.lse_off);
+    p.part_o = (float*)((char*)workspace + l.o_off);
+    if (mla::launch_plan(problem->batch, groups, seq_lens, prefix, stream) != hipSuccess ||
+        mla::launch_split(p, stream) != hipSuccess ||
+        mla::launch_combine_balanced(problem->batch, M, problem->d_latent, NB, prefix, p.part_o,
+                                     p.part_lse, problem->out_dtype, out, lse, stream) != hipSuccess)
+      return MLA_ERR_HIP;
+    return MLA_OK;
+  }
   if (S == 1) {
     p.write_final = true;
     p.out = out;
@@ -221,6 +303,70 @@ int mla_decode(const mla_problem* problem, const void* q_absorbed, const void* q
   if (mla::launch_split(p, stream) != hipSuccess) return MLA_ERR_HIP;
   return mla::launch_combine(problem->batch, S, rows, problem->d_latent, p.part_o, p.part_lse,
                              problem->out_dtype, out, lse, stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+int mla_balanced_workgroups(int32_t* num_workgroups) {
+  if (!num_workgroups) return MLA_ERR_INVALID_ARG;
+  const int32_t cus = device_cus();
+  if (cus <= 0) return MLA_ERR_HIP;
+  *num_workgroups = cus;
+  return MLA_OK;
+}
+
+int mla_plan_balanced(const mla_problem* problem, const int32_t* seq_lens, int32_t* tile_prefix,
+                      hipStream_t stream) {
+  const int rc = validate_problem(problem);
+  if (rc) return rc;
+  if (problem->batch == 0) return MLA_OK;
+  if (!seq_lens || !tile_prefix) return MLA_ERR_INVALID_ARG;
+  if (!balanced_size_ok(problem)) return MLA_ERR_UNSUPPORTED;
+  const int32_t M = problem->q_len * problem->num_heads;
+  const int32_t groups = (M + mla::kBalancedRows - 1) / mla::kBalancedRows;
+  return mla::launch_plan(problem->batch, groups, seq_lens, tile_prefix, stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+int mla_decode_split_balanced(const mla_problem* problem, const void* q_absorbed,
+                              const void* q_rope, const void* kv_pages, const float* kv_scales,
+                              const int32_t* page_table, const int32_t* seq_lens, float scale,
+                              int32_t num_workgroups, const int32_t* tile_prefix, void* out,
+                              float* lse, float* slot_o, float* slot_lse, hipStream_t stream) {
+  int rc = validate_problem(problem);
+  if (rc) return rc;
+  rc = validate_inputs(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table, seq_lens);
+  if (rc) return rc;
+  if (problem->batch == 0) return MLA_OK;
+  if (num_workgroups < 1 || !tile_prefix || !out || !slot_o || !slot_lse) return MLA_ERR_INVALID_ARG;
+  if (!balanced_size_ok(problem)) return MLA_ERR_UNSUPPORTED;
+  SplitParams p = make_params(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table,
+                              seq_lens, scale, 1);
+  if (mla::pick_kernel(p) == mla::Kernel::kGeneric) return MLA_ERR_UNSUPPORTED;
+  rc = run_checked_mode(problem, page_table, seq_lens, stream);
+  if (rc) return rc;
+  p.NB = num_workgroups;
+  p.tile_prefix = tile_prefix;
+  p.write_final = false;
+  p.out = out;
+  p.lse = lse;
+  p.part_o = slot_o;
+  p.part_lse = slot_lse;
+  return mla::launch_split(p, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_combine_balanced(const mla_problem* problem, int32_t num_workgroups,
+                         const int32_t* tile_prefix, const float* slot_o, const float* slot_lse,
+                         void* out, float* lse, hipStream_t stream) {
+  const int rc = validate_problem(problem);
+  if (rc) return rc;
+  if (problem->batch == 0) return MLA_OK;
+  if (num_workgroups < 1 || !tile_prefix || !slot_o || !slot_lse || !out) return MLA_ERR_INVALID_ARG;
+  const int32_t M = problem->q_len * problem->num_heads;
+  return mla::launch_combine_balanced(problem->batch, M, problem->d_latent, num_workgroups,
+                                      tile_prefix, slot_o, slot_lse, problem->out_dtype, out, lse,
+                                      stream) == hipSuccess
              ? MLA_OK
              : MLA_ERR_HIP;
 }

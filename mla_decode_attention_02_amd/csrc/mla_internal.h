@@ -27,7 +27,32 @@ struct SplitParams {
   float* part_o;               // [B, S, T*H, Dc] fp32 (!write_final)
   float* part_lse;             // [B, S, T*H] fp32 (!write_final)
   bool force_generic;          // run the VALU kernel even where the MFMA one applies
+  // Balanced work list (MFMA kernels only; NB == 0 selects uniform chunks):
+  // the 32-token tiles of all units (request, group of kBalancedRows rows)
+  // are cut into NB equal contiguous ranges, one per workgroup.
+  int32_t NB;
+  const int32_t* tile_prefix;  // [B * groups + 1] exclusive prefix of tiles per unit
 };
+
+// Rows per unit of the balanced work list (the MFMA kernels' workgroup rows).
+constexpr int32_t kBalancedRows = 128;
+
+// Number of units (request, row group) of the balanced work list.
+inline int64_t balanced_units(int32_t B, int32_t T, int32_t H) {
+  return (int64_t)B * (((int64_t)T * H + kBalancedRows - 1) / kBalancedRows);
+}
+
+// Balanced plan: tile_prefix[u] = sum over units v < u of ceil(L_b(v) / 32).
+hipError_t launch_plan(int32_t B, int32_t groups, const int32_t* seq_lens, int32_t* tile_prefix,
+                       hipStream_t stream);
+
+// Merge for the balanced work list: for each unit that spans several
+// workgroups, merge its partial slots into out/lse; units without tiles get
+// out = 0, lse = -inf; the others were written by the split kernel.
+hipError_t launch_combine_balanced(int32_t B, int32_t M, int32_t Dc, int32_t NB,
+                                   const int32_t* tile_prefix, const float* part_o,
+                                   const float* part_lse, int32_t out_dtype, void* out, float* lse,
+                                   hipStream_t stream);
 
 enum class Kernel { kMfmaBf16, kMfmaFp8, kGeneric };
 

@@ -351,24 +351,96 @@ mla_split_mfma(SplitParams p, int groups) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int h = lane >> 5, n = lane & 31;
 
-  // XCD-aware block mapping: consecutive hardware block ids go to different
-  // XCDs (id mod 8), so the row groups of one (request, chunk) unit are given
-  // ids 8 apart and share that XCD's L2 while they read the same pages.
-  const int x = blockIdx.x;
-  const int xcd = x & 7, slot = x >> 3;
-  const int k8 = slot / groups, g = slot - k8 * groups;
-  const int unit = 8 * k8 + xcd;
-  if (unit >= p.B * p.S) return;
-  const int b = unit / p.S, s = unit - b * p.S;
-
   const int M = p.T * p.H;
-  const int gr = g * kRows + 32 * wave + n;  // this lane's query row
+  // Work of this workgroup: a list of segments, each a run of 32-token tiles
+  // of one unit (request b, row group g).
+  //   Uniform chunks (p.NB == 0): one segment, chunk s of unit (b, g).  The
+  //   block mapping is XCD-aware: consecutive hardware block ids go to
+  //   different XCDs (id mod 8), so the row groups of one (request, chunk)
+  //   are given ids 8 apart and share that XCD's L2 while they read the same
+  //   pages.
+  //   Balanced (p.NB > 0): the units' tiles, laid end to end (unit-major,
+  //   prefix sums in p.tile_prefix), are cut into NB equal contiguous ranges,
+  //   one per workgroup; a range crosses unit boundaries freely, so every
+  //   workgroup gets the same number of tiles whatever the length mix.
+  int ub = 0, ug = 0, us = 0;
+  int64_t wx = 0, wx1 = 0;
+  int wu = 0, wk = 0;
+  if (p.NB == 0) {
+    const int x = blockIdx.x;
+    const int xcd = x & 7, slot = x >> 3;
+    const int k8 = slot / groups;
+    ug = slot - k8 * groups;
+    const int unit = 8 * k8 + xcd;
+    if (unit >= p.B * p.S) return;
+    ub = unit / p.S;
+    us = unit - ub * p.S;
+  } else {
+    const int U = p.B * groups;
+    const int64_t W = uniform_load(p.tile_prefix + U);
+    const int64_t nb = W < p.NB ? W : p.NB;  // no workgroup with an empty range
+    wk = blockIdx.x;
+    if (wk >= nb) return;
+    wx = wk * W / nb;
+    wx1 = (wk + 1) * W / nb;
+    // unit holding tile wx: the largest u with prefix[u] <= wx
+    int lo = 0, hi = U - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (uniform_load(p.tile_prefix + mid) <= wx) lo = mid;
+      else hi = mid - 1;
+    }
+    wu = lo;
+  }
+
+  for (bool more_segments = true; more_segments;) {
+  int b, g, L, cb, ce;
+  bool final_out;      // this segment is a whole unit: write the output itself
+  float* po_rows;      // partial rows of this segment (when !final_out)
+  float* pl_rows;
+  if (p.NB == 0) {
+    more_segments = false;
+    b = ub;
+    g = ug;
+    L = uniform_load(p.seq_lens + b);
+    chunk_span(L, p.S, p.P, us, &cb, &ce);
+    final_out = p.write_final;
+    const int64_t prow = ((int64_t)b * p.S + us) * M + (int64_t)g * kRows;
+    po_rows = p.part_o + prow * 512;
+    pl_rows = p.part_lse + prow;
+  } else {
+    int su = uniform_load(p.tile_prefix + wu), eu = uniform_load(p.tile_prefix + wu + 1);
+    while (eu <= wx) {  // skip units without tiles
+      ++wu;
+      su = eu;
+      eu = uniform_load(p.tile_prefix + wu + 1);
+    }
+    const int e = (int)(wx1 < eu ? wx1 : eu);
+    b = wu / groups;
+    g = wu - b * groups;
+    L = uniform_load(p.seq_lens + b);
+    cb = 32 * (int)(wx - su);
+    ce = 32 * (e - su);
+    if (ce > L) ce = L;
+    // Partial slots: [NB][2][kRows] rows.  Slot 0 holds the segment that
+    // continues a unit begun in an earlier workgroup, slot 1 the one that
+    // starts a unit and continues into later workgroups.
+    final_out = wx == su && e == eu;
+    const int64_t prow = ((int64_t)wk * 2 + (wx > su ? 0 : 1)) * kRows;
+    po_rows = p.part_o + prow * 512;
+    pl_rows = p.part_lse + prow;
+    wx = e;
+    ++wu;
+    more_segments = wx < wx1;
+  }
+  // the previous segment's waves are done with every stage before this one
+  // refills them
+  __syncthreads();
+
+  const int lr = 32 * wave + n;  // this lane's row within the group
+  const int gr = g * kRows + lr;  // this lane's query row
   const bool row_ok = gr < M;
   const int t = row_ok ? gr / p.H : 0;
-
-  const int L = uniform_load(p.seq_lens + b);
-  int cb, ce;
-  chunk_span(L, p.S, p.P, s, &cb, &ce);
   const int vis = p.causal ? (L - p.T + 1 + t) : L;
   const int lim = vis < ce ? vis : ce;  // tokens >= lim are masked for this row
 
@@ -726,8 +798,7 @@ mla_split_mfma(SplitParams p, int groups) {
   const float l_tot = half_swap_sum(l_part + l_part2);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_v = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : neg_inf();
-  if (!row_ok) return;
-  if (p.write_final) {
+  if (row_ok && final_out) {
     const int64_t obase = ((int64_t)b * M + gr) * 512;
 #pragma unroll
     for (int db = 0; db < 16; ++db)
@@ -743,9 +814,8 @@ mla_split_mfma(SplitParams p, int groups) {
         }
       }
     if (p.lse && h == 0) p.lse[(int64_t)b * M + gr] = lse_v;
-  } else {
-    const int64_t prow = ((int64_t)b * p.S + s) * M + gr;
-    float* po = p.part_o + prow * 512;
+  } else if (row_ok) {
+    float* po = po_rows + (int64_t)lr * 512;
 #pragma unroll
     for (int db = 0; db < 16; ++db)
 #pragma unroll
@@ -754,8 +824,9 @@ mla_split_mfma(SplitParams p, int groups) {
         *(floatx4*)(po + d) = floatx4{acc[db][4 * g4 + 0] * inv, acc[db][4 * g4 + 1] * inv,
                                       acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv};
       }
-    if (h == 0) p.part_lse[prow] = lse_v;
+    if (h == 0) pl_rows[lr] = lse_v;
   }
+  }  // segments
 }
 
 // ---------------------------------------------------- generic split kernel
@@ -910,6 +981,106 @@ mla_combine_kernel(int B, int S, int rows, int Dc, const float* __restrict__ po,
   if (lse && lane == 0) lse[idx] = wsum > 0.0f ? mx + __logf(wsum) : neg_inf();
 }
 
+// ------------------------------------------------------- balanced plan
+// tile_prefix[u] = tiles of the units before u, one unit = (request b, row
+// group g) with ceil(L_b / 32) tiles; tile_prefix[U] = all tiles.  One
+// workgroup: each thread sums a run of units, then a block-wide scan.
+__global__ void __launch_bounds__(1024)
+mla_plan_kernel(int B, int groups, const int32_t* __restrict__ seq_lens, int32_t* __restrict__ prefix) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int U = B * groups;
+  const int per = (U + 1023) / 1024;
+  const int u0 = tid * per < U ? tid * per : U;
+  const int u1 = u0 + per < U ? u0 + per : U;
+  auto tiles = [&](int u) {
+    const int L = seq_lens[u / groups];
+    return L > 0 ? (L + 31) >> 5 : 0;
+  };
+  int sum = 0;
+  for (int u = u0; u < u1; ++u) sum += tiles(u);
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - sum;
+  for (int u = u0; u < u1; ++u) {
+    prefix[u] = run;
+    run += tiles(u);
+  }
+  if (tid == 1023) prefix[U] = part[1023];
+}
+
+// Merge for the balanced work list (same arithmetic as mla_combine_kernel).
+// With W tiles cut into nb = min(NB, W) ranges [k W / nb, (k+1) W / nb),
+// tile x lies in range ceil((x+1) nb / W) - 1.  A unit whose tiles [su, eu)
+// lie in ranges k1 < k2 has its partials in slot 1 of workgroup k1 and in
+// slot 0 of workgroups k1+1 .. k2 (slot rows [k][2][kBalancedRows]).  One
+// wave per output row.
+__global__ void __launch_bounds__(256)
+mla_combine_balanced_kernel(int B, int M, int Dc, int NB, const int32_t* __restrict__ prefix,
+                            const float* __restrict__ po, const float* __restrict__ pl,
+                            int out_dtype, void* out, float* lse) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + wave;
+  if (idx >= (int64_t)B * M) return;
+  const int b = (int)(idx / M), r = (int)(idx - (int64_t)b * M);
+  const int groups = (M + kBalancedRows - 1) / kBalancedRows;
+  const int g = r / kBalancedRows, lr = r - g * kBalancedRows;
+  const int u = b * groups + g;
+  const int64_t W = prefix[B * groups];
+  const int64_t su = prefix[u], eu = prefix[u + 1];
+  const int64_t ob = idx * Dc;
+  auto store = [&](int d, float a) {
+    if (out_dtype == kBF16) ((__bf16*)out)[ob + d] = (__bf16)a;
+    else ((float*)out)[ob + d] = a;
+  };
+  if (su == eu) {  // no visible token: out = 0, lse = -inf
+    for (int d = lane; d < Dc; d += 64) store(d, 0.0f);
+    if (lse && lane == 0) lse[idx] = neg_inf();
+    return;
+  }
+  const int64_t nb = W < NB ? W : NB;
+  const int k1 = (int)(((su + 1) * nb + W - 1) / W - 1);
+  const int k2 = (int)((eu * nb + W - 1) / W - 1);
+  if (k1 == k2) return;  // written by the split kernel
+  const int ns = k2 - k1 + 1;
+  auto slot_row = [&](int j) -> int64_t {
+    const int64_t slot = j == 0 ? 2LL * k1 + 1 : 2LL * (k1 + j);
+    return slot * kBalancedRows + lr;
+  };
+  float mx = neg_inf();
+  for (int j = lane; j < ns; j += 64) mx = fmaxf(mx, pl[slot_row(j)]);
+  mx = wave_max(mx);
+  float wsum = 0.0f;
+  for (int j = lane; j < ns; j += 64) {
+    const float v = pl[slot_row(j)];
+    wsum += v == neg_inf() ? 0.0f : fast_exp2((v - mx) * kLog2e);
+  }
+  wsum = wave_sum(wsum);
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  for (int d = 4 * lane; d < Dc; d += 256) {
+    floatx4 a = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < ns; ++j) {
+      const int64_t pr = slot_row(j);
+      const float v = pl[pr];
+      if (v == neg_inf()) continue;
+      const float w = fast_exp2((v - mx) * kLog2e);
+      a += w * *(const floatx4*)(po + pr * Dc + d);
+    }
+    a *= inv;
+    if (out_dtype == kBF16)
+      *(bf16x4*)((__bf16*)out + ob + d) = bf16x4{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]};
+    else
+      *(floatx4*)((float*)out + ob + d) = a;
+  }
+  if (lse && lane == 0) lse[idx] = wsum > 0.0f ? mx + __logf(wsum) : neg_inf();
+}
+
 // ------------------------------------------------------------ gather hook
 __global__ void mla_gather_kernel(int D, int elt, int P, int MP, const char* __restrict__ kv,
                                   const int32_t* __restrict__ page_table, int n,
@@ -931,8 +1102,9 @@ hipError_t launch_mfma(const SplitParams& p, hipStream_t stream) {
   constexpr int kRows = 32 * WAVES;
   const int M = p.T * p.H;
   const int groups = (M + kRows - 1) / kRows;
+  static_assert(kRows == kBalancedRows, "balanced units are one workgroup of rows");
   const int units = p.B * p.S;
-  const int64_t blocks = 8LL * groups * ((units + 7) / 8);
+  const int64_t blocks = p.NB > 0 ? p.NB : 8LL * groups * ((units + 7) / 8);
   const size_t lds = (size_t)STAGES * Tile<FP8>::kStage + 8 * WAVES;  // + restart requests
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
@@ -980,6 +1152,23 @@ hipError_t launch_combine(int32_t B, int32_t S, int32_t rows, int32_t Dc, const 
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream, B, S,
                      rows, Dc, part_o, part_lse, out_dtype, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(int32_t B, int32_t groups, const int32_t* seq_lens, int32_t* tile_prefix,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, stream, B, groups, seq_lens, tile_prefix);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_balanced(int32_t B, int32_t M, int32_t Dc, int32_t NB,
+                                   const int32_t* tile_prefix, const float* part_o,
+                                   const float* part_lse, int32_t out_dtype, void* out, float* lse,
+                                   hipStream_t stream) {
+  const int64_t n = (int64_t)B * M;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_combine_balanced_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream,
+                     B, M, Dc, NB, tile_prefix, part_o, part_lse, out_dtype, out, lse);
   return hipGetLastError();
 }
 

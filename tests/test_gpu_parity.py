@@ -112,6 +112,38 @@ def test_empty_and_zero_length(mla):
     check_against_oracle(mla, inp, 2, "empty")
 
 
+# --------------------------------------------------- balanced work list
+# mla_decode with the library's own plan, on MFMA shapes where the uniform
+# plan would split, cuts all tiles into one equal range per compute unit.
+# Each case runs that path and, for comparison, the uniform plan.
+BALANCED_CASES = {
+    # zero-length requests between long and short ones
+    "mixed": small(1, batch=7, seq_lens=("fixed", (0, 1, 5000, 31, 0, 64, 2000)), decoys=4,
+                   index=40),
+    # one request over every workgroup: the merge takes one slot per workgroup
+    "one_long": small(1, batch=1, seq_lens=("fixed", (20000,)), decoys=2, index=41),
+    # fewer tiles than compute units: one tile per workgroup, the rest idle
+    "fewer_tiles_than_cus": small(1, batch=2, seq_lens=("fixed", (3, 40)), decoys=2, index=42),
+    # two row groups per request (64 heads x 4 drafts), causal chain
+    "causal_two_groups": small(3, batch=2, seq_lens=("fixed", (4, 3000)), decoys=2, index=43),
+    "fp8": small(4, batch=3, seq_lens=("fixed", (100, 7000, 64)), decoys=2, index=44),
+}
+
+
+@pytest.mark.parametrize("plan", ["balanced", "uniform"])
+@pytest.mark.parametrize("name", sorted(BALANCED_CASES))
+def test_balanced_work_list(mla, monkeypatch, name, plan):
+    if plan == "uniform":
+        monkeypatch.setenv("MLA_PLAN", "uniform")
+    w = BALANCED_CASES[name]
+    inp = synth.make_inputs(w)
+    check_against_oracle(mla, inp, 0, f"{name} {plan}")
+    if name == "mixed":
+        out, lse = run_decode(mla, inp)
+        assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
+        assert (out[4] == 0).all() and np.isneginf(lse[4]).all()
+
+
 # -------------------------------------------------------- bit-exact indexing
 
 @pytest.mark.parametrize("index", [0, 1, 4])
