@@ -255,7 +255,7 @@ def main():
 
     # mla_decode's own choice: the balanced work list when the library picks
     # the plan, the uniform plan would split, and the MFMA kernels serve the
-    # shape (MLA_PLAN=uniform turns it off).  Its three stages are called one
+    # shape (MLA_PLAN=uniform turns it off).  Its two stages are called one
     # by one so that the split kernel can be timed by itself.
     balanced = (S_req == 0 and S > 1 and w.d_latent == 512 and w.d_rope == 64
                 and w.q_dtype == "bf16" and w.kv_dtype in ("bf16", "fp8")
@@ -266,7 +266,6 @@ def main():
         prefix = torch.empty(B * groups + 1, dtype=torch.int32, device="cuda")
         slot_o = torch.empty((2 * nw, mla.BALANCED_ROWS, Dc), dtype=torch.float32, device="cuda")
         slot_l = torch.empty((2 * nw, mla.BALANCED_ROWS), dtype=torch.float32, device="cuda")
-        plan_args = [(ctypes.byref(prs), P(d["seq_lens"]), P(prefix), stream) for d in sets]
         bsplit_args = [(ctypes.byref(prs), P(d["q_abs"]), P(d["q_rope"]), P(d["kv"]),
                         P(d["kv_scales"]), P(d["page_table"]), P(d["seq_lens"]),
                         ctypes.c_float(scale), nw, P(prefix), P(out), P(lse), P(slot_o),
@@ -277,11 +276,7 @@ def main():
         if evs is not None:
             evs[0].record()
         if balanced:
-            # the plan is part of the step (it reads seq_lens on the device)
-            rc = lib.mla_plan_balanced(*plan_args[i % copies])
-            if evs is not None:
-                evs[3].record()
-            rc |= lib.mla_decode_split_balanced(*bsplit_args[i % copies])
+            rc = lib.mla_decode_split_balanced(*bsplit_args[i % copies])
             if evs is not None:
                 evs[1].record()
             rc |= lib.mla_combine_balanced(*bcomb_args)
@@ -309,16 +304,15 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    split_ms = [e[3 if balanced else 0].elapsed_time(e[1]) for e in events]
+    split_ms = [e[0].elapsed_time(e[1]) for e in events]
     comb_ms = [e[1].elapsed_time(e[2]) for e in events]
-    plan_ms = [e[0].elapsed_time(e[3]) for e in events] if balanced else [0.0]
     ms_per_step = wall * 1e3 / args.steps
 
     L = inp["seq_lens"]
@@ -363,7 +357,6 @@ def main():
                    "kv_copies_rotated": copies, "parallelism": "single GPU"},
         "tokens_per_s": round(tokens_per_s, 1),
         "kv_gbs_unique": round(alg_path["kv_unique"] / (ms_per_step / 1e3) / 1e9, 2),
-        "plan_ms": round(float(np.mean(plan_ms)), 5),
         "split_ms": round(split_avg, 5), "combine_ms": round(float(np.mean(comb_ms)), 5),
         "roofline": roof, "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_source_hash(),

@@ -169,16 +169,17 @@ int mla_combine(int32_t batch, int32_t num_splits, int32_t rows, int32_t d_laten
                 void* out, float* lse, hipStream_t stream);
 
 /*
- * The balanced work list stage by stage (mla_decode() runs these three, with
+ * The balanced work list stage by stage (mla_decode() runs these two, with
  * num_workgroups from mla_balanced_workgroups(), when it picks that plan).
  * A unit is (request b, row group g): the T*H rows of a request in groups of
- * 128 (U = B * ceil(T*H / 128) units), with ceil(L_b / 32) tiles of 32
- * tokens.  With W tiles in all, workgroup k of nb = min(num_workgroups, W)
- * takes the tiles [k W / nb, (k+1) W / nb) of the units laid end to end;
- * each maximal run of one unit's tiles in that range is a segment.  This is
- * the code-audit article's two-stage split/reduce decode with the chunk
- * bounds chosen for equal work per compute unit instead of equal chunks per
- * request.
+ * 128 (U = B * ceil(T*H / 128) units, u = b * ceil(T*H / 128) + g), with
+ * ceil(L_b / 32) tiles of 32 tokens.  With W tiles in all, workgroup k of
+ * nb = min(num_workgroups, W) takes the tiles [k W / nb, (k+1) W / nb) of
+ * the units laid end to end; each maximal run of one unit's tiles in that
+ * range is a segment.  This is the code-audit article's two-stage
+ * split/reduce decode with the chunk bounds chosen for equal work per
+ * compute unit instead of equal chunks per request.  The plan is computed on
+ * the device from seq_lens (no host synchronisation).
  */
 
 /* Workgroups of the balanced work list on the current device (its compute
@@ -186,23 +187,16 @@ int mla_combine(int32_t batch, int32_t num_splits, int32_t rows, int32_t d_laten
 int mla_balanced_workgroups(int32_t* num_workgroups);
 
 /*
- * Plan: tile_prefix [U + 1] int32 (device) gets tile_prefix[u] = tiles of
- * units v < u and tile_prefix[U] = W, from seq_lens [B] on the device (no
- * host synchronisation).  MLA_ERR_UNSUPPORTED if W could exceed 2^30.
- */
-int mla_plan_balanced(const mla_problem* problem, const int32_t* seq_lens, int32_t* tile_prefix,
-                      hipStream_t stream);
-
-/*
  * Split stage of the balanced work list on the MFMA kernels (Dc 512, Dr 64,
  * bf16 queries, bf16 or FP8 KV, P a multiple of 32, scale > 0; else
- * MLA_ERR_UNSUPPORTED).  Inputs as for mla_decode(); tile_prefix from
- * mla_plan_balanced() on the same seq_lens.  A segment that is a whole unit
- * writes its rows of out [B, T, H, Dc] (out_dtype) and lse (if not NULL)
- * directly.  Any other segment writes its normalised fp32 partial and
- * natural-log lse to a slot: slot 2k if it continues a unit begun in an
- * earlier workgroup, 2k + 1 if it starts a unit that continues in later
- * ones, with
+ * MLA_ERR_UNSUPPORTED, as when W could exceed 2^30).  Inputs as for
+ * mla_decode().  Writes tile_prefix [U + 1] int32 (tile_prefix[u] = tiles of
+ * the units before u, tile_prefix[U] = W) for the merge stage.  A segment
+ * that is a whole unit writes its rows of out [B, T, H, Dc] (out_dtype) and
+ * lse (if not NULL) directly.  Any other segment writes its normalised fp32
+ * partial and natural-log lse to a slot: slot 2k if it continues a unit
+ * begun in an earlier workgroup, 2k + 1 if it starts a unit that continues
+ * in later ones, with
  *   slot_o   [2 * num_workgroups, 128, Dc] fp32 (row = unit row r - 128 g)
  *   slot_lse [2 * num_workgroups, 128] fp32
  * Slots and out rows that no segment writes are left untouched.
@@ -210,14 +204,15 @@ int mla_plan_balanced(const mla_problem* problem, const int32_t* seq_lens, int32
 int mla_decode_split_balanced(const mla_problem* problem, const void* q_absorbed,
                               const void* q_rope, const void* kv_pages, const float* kv_scales,
                               const int32_t* page_table, const int32_t* seq_lens, float scale,
-                              int32_t num_workgroups, const int32_t* tile_prefix, void* out,
+                              int32_t num_workgroups, int32_t* tile_prefix, void* out,
                               float* lse, float* slot_o, float* slot_lse, hipStream_t stream);
 
 /*
- * Merge stage of the balanced work list: for every unit whose tiles span
- * workgroups k1 < k2, merge slot 2 k1 + 1 and slots 2k (k1 < k <= k2) as
- * mla_combine() does into out/lse; units without tiles get out = 0 and
- * lse = -inf; other units' rows are left as the split stage wrote them.
+ * Merge stage of the balanced work list, after mla_decode_split_balanced()
+ * with the same num_workgroups: for every unit whose tiles span workgroups
+ * k1 < k2, merge slot 2 k1 + 1 and slots 2k (k1 < k <= k2) as mla_combine()
+ * does into out/lse; units without tiles get out = 0 and lse = -inf; other
+ * units' rows are left as the split stage wrote them.
  */
 int mla_combine_balanced(const mla_problem* problem, int32_t num_workgroups,
                          const int32_t* tile_prefix, const float* slot_o, const float* slot_lse,

@@ -22,7 +22,7 @@ MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE = -1, -2, -3
 MLA_ERR_HIP, MLA_ERR_CHECK = -4, -5
 
 EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_decode_split",
-           "mla_combine", "mla_balanced_workgroups", "mla_plan_balanced",
+           "mla_combine", "mla_balanced_workgroups",
            "mla_decode_split_balanced", "mla_combine_balanced", "mla_gather_rows",
            "mla_check_tables", "mla_status_string")
 
@@ -63,7 +63,6 @@ def library():
     lib.mla_decode_split.argtypes = [PP, P, P, P, P, P, P, ctypes.c_float, i32, P, P, P]
     lib.mla_combine.argtypes = [i32, i32, i32, i32, P, P, i32, P, P, P]
     lib.mla_balanced_workgroups.argtypes = [ctypes.POINTER(i32)]
-    lib.mla_plan_balanced.argtypes = [PP, P, P, P]
     lib.mla_decode_split_balanced.argtypes = [PP, P, P, P, P, P, P, ctypes.c_float, i32, P, P, P,
                                               P, P, P]
     lib.mla_combine_balanced.argtypes = [PP, i32, P, P, P, P, P, P]
@@ -224,31 +223,18 @@ def balanced_workgroups():
     return int(n.value)
 
 
-def plan_balanced(problem, seq_lens, tile_prefix=None):
-    """Balanced plan: tile_prefix [U + 1] int32 (exclusive prefix of tiles per unit)."""
-    dev = seq_lens.device
-    _require(seq_lens, "seq_lens", dev, dtype=torch.int32, ndim=1)
-    groups = -(-problem.q_len * problem.num_heads // BALANCED_ROWS)
-    n = problem.batch * groups + 1
-    if tile_prefix is None:
-        tile_prefix = torch.empty(n, dtype=torch.int32, device=dev)
-    _require(tile_prefix, "tile_prefix", dev, dtype=torch.int32)
-    if tile_prefix.numel() < n:
-        raise ValueError("tile_prefix too small")
-    _check(library().mla_plan_balanced(ctypes.byref(problem), _ptr(seq_lens), _ptr(tile_prefix),
-                                       _stream()), "mla_plan_balanced")
-    return tile_prefix
-
-
 def decode_split_balanced(problem, q_abs, q_rope, kv_pages, page_table, seq_lens, scale,
                           num_workgroups, tile_prefix, out, lse, slot_o, slot_lse, *,
                           kv_scales=None):
-    """Split stage of the balanced work list (writes whole units to out/lse, other
-    segments to slot_o [2 nw, 128, Dc] / slot_lse [2 nw, 128])."""
+    """Split stage of the balanced work list: writes tile_prefix [U + 1], whole units
+    to out/lse and other segments to slot_o [2 nw, 128, Dc] / slot_lse [2 nw, 128]."""
     _validate(q_abs, q_rope, kv_pages, page_table, seq_lens, kv_scales)
     dev = q_abs.device
     nw = int(num_workgroups)
     _require(tile_prefix, "tile_prefix", dev, dtype=torch.int32)
+    groups = -(-problem.q_len * problem.num_heads // BALANCED_ROWS)
+    if tile_prefix.numel() < problem.batch * groups + 1:
+        raise ValueError("tile_prefix too small")
     _require(out, "out", dev, dtype=_torch_dtype(problem.out_dtype))
     _require(lse, "lse", dev, dtype=torch.float32)
     _require(slot_o, "slot_o", dev, dtype=torch.float32)

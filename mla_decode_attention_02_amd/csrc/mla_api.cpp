@@ -269,11 +269,10 @@ int mla_decode(const mla_problem* problem, const void* q_absorbed, const void* q
   SplitParams p = make_params(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table,
                               seq_lens, scale, S);
   if (NB > 0 && mla::pick_kernel(p) != mla::Kernel::kGeneric) {
-    // the stages of mla_plan_balanced, mla_decode_split_balanced and
-    // mla_combine_balanced, arguments already validated
+    // the stages of mla_decode_split_balanced and mla_combine_balanced,
+    // arguments already validated
     const BalancedLayout l = balanced_layout(problem, NB);
     const int32_t M = problem->q_len * problem->num_heads;
-    const int32_t groups = (M + mla::kBalancedRows - 1) / mla::kBalancedRows;
     int32_t* prefix = (int32_t*)((char*)workspace + l.prefix_off);
     p.NB = NB;
     p.tile_prefix = prefix;
@@ -282,8 +281,7 @@ int mla_decode(const mla_problem* problem, const void* q_absorbed, const void* q
     p.lse = lse;
     p.part_lse = (float*)((char*)workspace + l.lse_off);
     p.part_o = (float*)((char*)workspace + l.o_off);
-    if (mla::launch_plan(problem->batch, groups, seq_lens, prefix, stream) != hipSuccess ||
-        mla::launch_split(p, stream) != hipSuccess ||
+    if (mla::launch_split(p, stream) != hipSuccess ||
         mla::launch_combine_balanced(problem->batch, M, problem->d_latent, NB, prefix, p.part_o,
                                      p.part_lse, problem->out_dtype, out, lse, stream) != hipSuccess)
       return MLA_ERR_HIP;
@@ -315,24 +313,10 @@ int mla_balanced_workgroups(int32_t* num_workgroups) {
   return MLA_OK;
 }
 
-int mla_plan_balanced(const mla_problem* problem, const int32_t* seq_lens, int32_t* tile_prefix,
-                      hipStream_t stream) {
-  const int rc = validate_problem(problem);
-  if (rc) return rc;
-  if (problem->batch == 0) return MLA_OK;
-  if (!seq_lens || !tile_prefix) return MLA_ERR_INVALID_ARG;
-  if (!balanced_size_ok(problem)) return MLA_ERR_UNSUPPORTED;
-  const int32_t M = problem->q_len * problem->num_heads;
-  const int32_t groups = (M + mla::kBalancedRows - 1) / mla::kBalancedRows;
-  return mla::launch_plan(problem->batch, groups, seq_lens, tile_prefix, stream) == hipSuccess
-             ? MLA_OK
-             : MLA_ERR_HIP;
-}
-
 int mla_decode_split_balanced(const mla_problem* problem, const void* q_absorbed,
                               const void* q_rope, const void* kv_pages, const float* kv_scales,
                               const int32_t* page_table, const int32_t* seq_lens, float scale,
-                              int32_t num_workgroups, const int32_t* tile_prefix, void* out,
+                              int32_t num_workgroups, int32_t* tile_prefix, void* out,
                               float* lse, float* slot_o, float* slot_lse, hipStream_t stream) {
   int rc = validate_problem(problem);
   if (rc) return rc;

@@ -31,7 +31,8 @@ struct SplitParams {
   // the 32-token tiles of all units (request, group of kBalancedRows rows)
   // are cut into NB equal contiguous ranges, one per workgroup.
   int32_t NB;
-  const int32_t* tile_prefix;  // [B * groups + 1] exclusive prefix of tiles per unit
+  int32_t* tile_prefix;        // [B * groups + 1] exclusive prefix of tiles per unit,
+                               // written by workgroup 0 for the merge
 };
 
 // Rows per unit of the balanced work list (the MFMA kernels' workgroup rows).
@@ -41,10 +42,6 @@ constexpr int32_t kBalancedRows = 128;
 inline int64_t balanced_units(int32_t B, int32_t T, int32_t H) {
   return (int64_t)B * (((int64_t)T * H + kBalancedRows - 1) / kBalancedRows);
 }
-
-// Balanced plan: tile_prefix[u] = sum over units v < u of ceil(L_b(v) / 32).
-hipError_t launch_plan(int32_t B, int32_t groups, const int32_t* seq_lens, int32_t* tile_prefix,
-                       hipStream_t stream);
 
 // Merge for the balanced work list: for each unit that spans several
 // workgroups, merge its partial slots into out/lse; units without tiles get

@@ -188,10 +188,20 @@ __device__ __forceinline__ uint32_t lds_addr(LDS_AS const void* p) {
 // Direct-to-LDS load number q (0 <= q < loads_per_wave) of one tile for this
 // wave.  `tile_g` is the first row of the tile in HBM (32 rows, contiguous
 // within one page).
+// Lane id passed through an empty asm statement: offsets computed from it are
+// recomputed where they are used (a few VALU operations) instead of being
+// kept live through the tile loop, where registers are the scarce resource.
+__device__ __forceinline__ int fresh_lane() {
+  int l = __lane_id();
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 template <bool FP8, int WAVES>
 __device__ __forceinline__ void issue_piece(const char* tile_g, const float* scale_g,
-                                            LDS_AS char* st, int wave, int lane, int q) {
+                                            LDS_AS char* st, int wave, int /*lane*/, int q) {
   using G = Tile<FP8>;
+  const int lane = fresh_lane();
   if constexpr (!FP8) {
     if (q < 32 / WAVES) {  // latent rows
       const int r = wave + q * WAVES;
@@ -364,8 +374,8 @@ mla_split_mfma(SplitParams p, int groups) {
   //   one per workgroup; a range crosses unit boundaries freely, so every
   //   workgroup gets the same number of tiles whatever the length mix.
   int ub = 0, ug = 0, us = 0;
-  int64_t wx = 0, wx1 = 0;
-  int wu = 0, wk = 0;
+  int wx = 0, wx1 = 0;
+  int wu = 0, wk = 0, wsu = 0;  // balanced: current unit and its first tile
   if (p.NB == 0) {
     const int x = blockIdx.x;
     const int xcd = x & 7, slot = x >> 3;
@@ -376,28 +386,77 @@ mla_split_mfma(SplitParams p, int groups) {
     ub = unit / p.S;
     us = unit - ub * p.S;
   } else {
+    // Plan, in every workgroup: each thread sums the tiles of a run of
+    // units, a block-wide scan gives the runs' offsets, and the thread whose
+    // run holds this workgroup's first tile finds its unit.  Workgroup 0
+    // also writes the prefix sums for the merge.
+    volatile LDS_AS int* ps = (volatile LDS_AS int*)(smem + STAGES * G::kStage + 8 * WAVES);
     const int U = p.B * groups;
-    const int64_t W = uniform_load(p.tile_prefix + U);
+    const int per = (U + 64 * WAVES - 1) / (64 * WAVES);
+    const int u0 = tid * per < U ? tid * per : U;
+    const int u1 = u0 + per < U ? u0 + per : U;
+    auto unit_tiles = [&](int u) {
+      const int Lu = p.seq_lens[u / groups];
+      return Lu > 0 ? (Lu + 31) >> 5 : 0;
+    };
+    int run_sum = 0;
+    for (int u = u0; u < u1; ++u) run_sum += unit_tiles(u);
+    int incl = run_sum;  // inclusive scan within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) ps[wave] = incl;
+    __syncthreads();
+    int W = 0, before = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const int v = ps[w];
+      before += w < wave ? v : 0;
+      W += v;
+    }
+    W = __builtin_amdgcn_readfirstlane(W);  // the same in every lane
+    const int excl = before + incl - run_sum;
+    if (blockIdx.x == 0) {
+      int run = excl;
+      for (int u = u0; u < u1; ++u) {
+        p.tile_prefix[u] = run;
+        run += unit_tiles(u);
+      }
+      if (tid == 0) p.tile_prefix[U] = W;
+    }
     const int64_t nb = W < p.NB ? W : p.NB;  // no workgroup with an empty range
     wk = blockIdx.x;
     if (wk >= nb) return;
-    wx = wk * W / nb;
-    wx1 = (wk + 1) * W / nb;
-    // unit holding tile wx: the largest u with prefix[u] <= wx
-    int lo = 0, hi = U - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (uniform_load(p.tile_prefix + mid) <= wx) lo = mid;
-      else hi = mid - 1;
+    // (W < 2^30, so the bounds fit in int32; read back as wave-uniform values)
+    wx = __builtin_amdgcn_readfirstlane((int)(wk * (int64_t)W / nb));
+    wx1 = __builtin_amdgcn_readfirstlane((int)((wk + 1) * (int64_t)W / nb));
+    if (excl <= wx && wx < excl + run_sum) {
+      int run = excl, fu = u0, fr = excl;
+      bool found = false;
+      for (int u = u0; u < u1; ++u) {
+        const int tu = unit_tiles(u);
+        const bool hit = !found && wx < run + tu;
+        fu = hit ? u : fu;
+        fr = hit ? run : fr;
+        found = found || hit;
+        run += tu;
+      }
+      ps[WAVES] = fu;
+      ps[WAVES + 1] = fr;
     }
-    wu = lo;
+    __syncthreads();
+    wu = __builtin_amdgcn_readfirstlane(ps[WAVES]);
+    wsu = __builtin_amdgcn_readfirstlane(ps[WAVES + 1]);
   }
 
   for (bool more_segments = true; more_segments;) {
   int b, g, L, cb, ce;
-  bool final_out;      // this segment is a whole unit: write the output itself
-  float* po_rows;      // partial rows of this segment (when !final_out)
-  float* pl_rows;
+  // destination: rows [drow, drow + kRows) of out/lse when the segment is a
+  // whole unit (final_out), else of the partial buffers
+  bool final_out;
+  int64_t drow;
   if (p.NB == 0) {
     more_segments = false;
     b = ub;
@@ -405,20 +464,20 @@ mla_split_mfma(SplitParams p, int groups) {
     L = uniform_load(p.seq_lens + b);
     chunk_span(L, p.S, p.P, us, &cb, &ce);
     final_out = p.write_final;
-    const int64_t prow = ((int64_t)b * p.S + us) * M + (int64_t)g * kRows;
-    po_rows = p.part_o + prow * 512;
-    pl_rows = p.part_lse + prow;
+    drow = final_out ? (int64_t)b * M + (int64_t)g * kRows
+                     : ((int64_t)b * p.S + us) * M + (int64_t)g * kRows;
   } else {
-    int su = uniform_load(p.tile_prefix + wu), eu = uniform_load(p.tile_prefix + wu + 1);
-    while (eu <= wx) {  // skip units without tiles
+    int su = wsu, eu;
+    for (;;) {  // skip units without tiles
+      b = wu / groups;
+      L = uniform_load(p.seq_lens + b);
+      eu = su + (L > 0 ? (L + 31) >> 5 : 0);
+      if (eu > wx) break;
       ++wu;
       su = eu;
-      eu = uniform_load(p.tile_prefix + wu + 1);
     }
     const int e = (int)(wx1 < eu ? wx1 : eu);
-    b = wu / groups;
     g = wu - b * groups;
-    L = uniform_load(p.seq_lens + b);
     cb = 32 * (int)(wx - su);
     ce = 32 * (e - su);
     if (ce > L) ce = L;
@@ -426,11 +485,11 @@ mla_split_mfma(SplitParams p, int groups) {
     // continues a unit begun in an earlier workgroup, slot 1 the one that
     // starts a unit and continues into later workgroups.
     final_out = wx == su && e == eu;
-    const int64_t prow = ((int64_t)wk * 2 + (wx > su ? 0 : 1)) * kRows;
-    po_rows = p.part_o + prow * 512;
-    pl_rows = p.part_lse + prow;
+    drow = final_out ? (int64_t)b * M + (int64_t)g * kRows
+                     : ((int64_t)wk * 2 + (wx > su ? 0 : 1)) * kRows;
     wx = e;
     ++wu;
+    wsu = eu;
     more_segments = wx < wx1;
   }
   // the previous segment's waves are done with every stage before this one
@@ -667,20 +726,19 @@ mla_split_mfma(SplitParams p, int groups) {
       for (int c = 0; c < 16; ++c) tscv[c] = 1.0f;
     }
     if constexpr (!FP8) {
-      const LDS_AS char* bp[2][2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int r0 = 16 * q + 8 * h + (sl >> 2);
-        const int cpart = 2 * dh + ((sl & 3) >> 1);
-        bp[q][0] = sv + G::lat_base(r0) + 16 * cpart + 8 * (sl & 1);
-        bp[q][1] = sv + G::lat_base(r0 + 4) + 16 * cpart + 8 * (sl & 1);
-      }
+      // Rows r0 = 8h + (sl >> 2) (+4, +16, +20) of the tile: r0 & 15 <= 11,
+      // so B(r0 + 4) = B(r0) + 273 and B(r0 + 16) = B(r0) + 1088, and all
+      // four reads are one base register plus immediates.
+      const int ln = fresh_lane(), lh = ln >> 5, lsl = ln & 15, ldh = (ln >> 4) & 1;
+      const LDS_AS char* vb =
+          sv + G::lat_base(8 * lh + (lsl >> 2)) + 16 * (2 * ldh + ((lsl & 3) >> 1)) + 8 * (lsl & 1);
       // whole-vector reinterpretation of the two transposed reads
       // (element-wise bf16 inserts were miscompiled into a broadcast)
       auto vread = [&](int x2) -> bf16x8 {
         const int q = x2 >> 4, db = x2 & 15;
-        const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(bp[q][0] + 64 * db));
-        const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(bp[q][1] + 64 * db));
+        const LDS_AS char* b0 = vb + 16 * 1088 * q + 64 * db;
+        const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)b0);
+        const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(b0 + 16 * 273));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       constexpr int kAhead = 3;  // value operands in flight ahead of their MFMA
@@ -696,14 +754,13 @@ mla_split_mfma(SplitParams p, int groups) {
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      const LDS_AS char* bp[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int r0 = 16 * q + 8 * h + (sl >> 1);
-        bp[q] = sv + G::lat_base(r0) + 16 * (dh ^ G::xlat(r0)) + 8 * (sl & 1);
-      }
+      // rows r0 = 8h + (sl >> 1) and r0 + 16 share a block, 512 B apart,
+      // with the same chunk swizzle: one base register plus immediates
+      const int ln = fresh_lane(), lsl = ln & 15, ldh = (ln >> 4) & 1;
+      const int r0 = 8 * (ln >> 5) + (lsl >> 1);
+      const LDS_AS char* vb = sv + G::lat_base(r0) + 16 * (ldh ^ G::xlat(r0)) + 8 * (lsl & 1);
       auto vread = [&](int x2) -> intx2 {
-        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS intx2*)(bp[x2 >> 4] + 32 * (x2 & 15)));
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS intx2*)(vb + 512 * (x2 >> 4) + 32 * (x2 & 15)));
       };
       constexpr int kAhead = 3;
       intx2 ring[kAhead];
@@ -798,33 +855,32 @@ mla_split_mfma(SplitParams p, int groups) {
   const float l_tot = half_swap_sum(l_part + l_part2);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_v = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : neg_inf();
-  if (row_ok && final_out) {
-    const int64_t obase = ((int64_t)b * M + gr) * 512;
+  // one straight store sequence per destination kind: normalised rows of
+  // out (bf16 or fp32) for a whole unit, fp32 partial rows otherwise
+  auto store_rows = [&](auto* dst, auto cvt) {
 #pragma unroll
     for (int db = 0; db < 16; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * db + 8 * g4 + 4 * h;
-        const float o0 = acc[db][4 * g4 + 0] * inv, o1 = acc[db][4 * g4 + 1] * inv;
-        const float o2 = acc[db][4 * g4 + 2] * inv, o3 = acc[db][4 * g4 + 3] * inv;
-        if (p.out_dtype == kBF16) {
-          *(bf16x4*)((__bf16*)p.out + obase + d) = bf16x4{(__bf16)o0, (__bf16)o1, (__bf16)o2, (__bf16)o3};
-        } else {
-          *(floatx4*)((float*)p.out + obase + d) = floatx4{o0, o1, o2, o3};
-        }
-      }
-    if (p.lse && h == 0) p.lse[(int64_t)b * M + gr] = lse_v;
-  } else if (row_ok) {
-    float* po = po_rows + (int64_t)lr * 512;
-#pragma unroll
-    for (int db = 0; db < 16; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * db + 8 * g4 + 4 * h;
-        *(floatx4*)(po + d) = floatx4{acc[db][4 * g4 + 0] * inv, acc[db][4 * g4 + 1] * inv,
-                                      acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv};
-      }
-    if (h == 0) pl_rows[lr] = lse_v;
+      for (int g4 = 0; g4 < 4; ++g4)
+        *(decltype(cvt(floatx4{}))*)(dst + 32 * db + 8 * g4 + 4 * h) =
+            cvt(floatx4{acc[db][4 * g4 + 0] * inv, acc[db][4 * g4 + 1] * inv,
+                        acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv});
+  };
+  auto to_bf16 = [](floatx4 v) { return bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]}; };
+  auto to_f32 = [](floatx4 v) { return v; };
+  // (the destination row is taken through an empty asm statement so that
+  // no address of it is computed before, and kept live through, the loop)
+  asm volatile("" : "+s"(drow));
+  const int64_t orow = drow + lr;
+  if (row_ok) {
+    if (final_out) {
+      if (p.out_dtype == kBF16) store_rows((__bf16*)p.out + orow * 512, to_bf16);
+      else store_rows((float*)p.out + orow * 512, to_f32);
+      if (p.lse && h == 0) p.lse[orow] = lse_v;
+    } else {
+      store_rows(p.part_o + orow * 512, to_f32);
+      if (h == 0) p.part_lse[orow] = lse_v;
+    }
   }
   }  // segments
 }
@@ -927,94 +983,105 @@ __global__ void __launch_bounds__(256) mla_split_generic(SplitParams p) {
 }
 
 // ----------------------------------------------------------- combine kernel
-// One wavefront per (request, row): weights w_k = exp(lse_k - max lse),
-// out = sum_k w_k o_k / sum_k w_k; chunks with lse = -inf are skipped (their
-// partial rows are never read).
-__global__ void __launch_bounds__(256)
-mla_combine_kernel(int B, int S, int rows, int Dc, const float* __restrict__ po,
-                   const float* __restrict__ pl, int out_dtype, void* out, float* lse) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t idx = (int64_t)blockIdx.x * 4 + wave;
-  if (idx >= (int64_t)B * rows) return;
-  const int b = (int)(idx / rows), r = (int)(idx - (int64_t)b * rows);
+// Log-sum-exp merge of one output row (one wavefront) from ns partial rows,
+// partial j at row slot_row(j) of po / pl: M = max_j lse_j, w_j =
+// exp(lse_j - M), out = sum_j w_j o_j / sum_j w_j, lse = M + ln sum_j w_j.
+// Partials with lse = -inf weigh nothing (their rows may hold anything, NaN
+// included); with none left, out = 0 and lse = -inf.  The normalised weights of 64 partials
+// at a time sit one per lane and are broadcast by shuffles, and each lane
+// accumulates 8 columns, so several partial rows are in flight per wave.
+template <typename SlotRow>
+__device__ __forceinline__ void merge_row(int ns, int Dc, SlotRow slot_row, const float* __restrict__ po,
+                                          const float* __restrict__ pl, int out_dtype, void* out,
+                                          int64_t out_row, float* lse) {
+  const int lane = threadIdx.x & 63;
   float mx = neg_inf();
-  for (int k = lane; k < S; k += 64) mx = fmaxf(mx, pl[((int64_t)b * S + k) * rows + r]);
+  for (int j = lane; j < ns; j += 64) mx = fmaxf(mx, pl[slot_row(j)]);
   mx = wave_max(mx);
   float wsum = 0.0f;
-  for (int k = lane; k < S; k += 64) {
-    const float v = pl[((int64_t)b * S + k) * rows + r];
+  for (int j = lane; j < ns; j += 64) {
+    const float v = pl[slot_row(j)];
     wsum += v == neg_inf() ? 0.0f : fast_exp2((v - mx) * kLog2e);
   }
   wsum = wave_sum(wsum);
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  const int64_t ob = idx * Dc;
+  const int64_t ob = out_row * Dc;
+  auto put4 = [&](int d, floatx4 a) {
+    if (out_dtype == kBF16)
+      *(bf16x4*)((__bf16*)out + ob + d) = bf16x4{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]};
+    else
+      *(floatx4*)((float*)out + ob + d) = a;
+  };
   if ((Dc & 3) == 0) {
-    for (int d = 4 * lane; d < Dc; d += 256) {
-      floatx4 a = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-      for (int k = 0; k < S; ++k) {
-        const int64_t pr = ((int64_t)b * S + k) * rows + r;
-        const float v = pl[pr];
-        if (v == neg_inf()) continue;
-        const float w = fast_exp2((v - mx) * kLog2e);
-        a += w * *(const floatx4*)(po + pr * Dc + d);
+    for (int d0 = 0; d0 < Dc; d0 += 512) {
+      const int da = d0 + 4 * lane, db = da + 256;
+      const bool oka = da < Dc, okb = db < Dc;
+      floatx4 a = floatx4{0.0f, 0.0f, 0.0f, 0.0f}, c = a;
+      for (int j0 = 0; j0 < ns; j0 += 64) {
+        float wj = 0.0f;
+        if (j0 + lane < ns) {
+          const float v = pl[slot_row(j0 + lane)];
+          wj = v == neg_inf() ? 0.0f : fast_exp2((v - mx) * kLog2e) * inv;
+        }
+        const int cnt = ns - j0 < 64 ? ns - j0 : 64;
+        // four partial rows per round, all loads issued before the first
+        // use; every slot row lies inside the partial buffer, so rows are
+        // read unconditionally (a round past the end re-reads the last one)
+        // and a zero-weight row is dropped by a select, never multiplied in
+        for (int jj = 0; jj < cnt; jj += 4) {
+          floatx4 x[4], y[4];
+          float w[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int j = jj + q < cnt ? jj + q : cnt - 1;
+            w[q] = jj + q < cnt ? __shfl(wj, j, 64) : 0.0f;
+            const float* row = po + slot_row(j0 + j) * Dc;
+            x[q] = oka ? *(const floatx4*)(row + da) : floatx4{};
+            y[q] = okb ? *(const floatx4*)(row + db) : floatx4{};
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bool live = w[q] != 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              a[e] = live ? __builtin_fmaf(w[q], x[q][e], a[e]) : a[e];
+              c[e] = live ? __builtin_fmaf(w[q], y[q][e], c[e]) : c[e];
+            }
+          }
+        }
       }
-      a *= inv;
-      if (out_dtype == kBF16)
-        *(bf16x4*)((__bf16*)out + ob + d) = bf16x4{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]};
-      else
-        *(floatx4*)((float*)out + ob + d) = a;
+      if (oka) put4(da, a);
+      if (okb) put4(db, c);
     }
   } else {
     for (int d = lane; d < Dc; d += 64) {
       float a = 0.0f;
-      for (int k = 0; k < S; ++k) {
-        const int64_t pr = ((int64_t)b * S + k) * rows + r;
-        const float v = pl[pr];
+      for (int j = 0; j < ns; ++j) {
+        const float v = pl[slot_row(j)];
         if (v == neg_inf()) continue;
-        a += fast_exp2((v - mx) * kLog2e) * po[pr * Dc + d];
+        a += fast_exp2((v - mx) * kLog2e) * inv * po[slot_row(j) * Dc + d];
       }
-      a *= inv;
       if (out_dtype == kBF16) ((__bf16*)out)[ob + d] = (__bf16)a;
       else ((float*)out)[ob + d] = a;
     }
   }
-  if (lse && lane == 0) lse[idx] = wsum > 0.0f ? mx + __logf(wsum) : neg_inf();
+  if (lse && lane == 0) lse[out_row] = wsum > 0.0f ? mx + __logf(wsum) : neg_inf();
 }
 
-// ------------------------------------------------------- balanced plan
-// tile_prefix[u] = tiles of the units before u, one unit = (request b, row
-// group g) with ceil(L_b / 32) tiles; tile_prefix[U] = all tiles.  One
-// workgroup: each thread sums a run of units, then a block-wide scan.
-__global__ void __launch_bounds__(1024)
-mla_plan_kernel(int B, int groups, const int32_t* __restrict__ seq_lens, int32_t* __restrict__ prefix) {
-  __shared__ int part[1024];
-  const int tid = threadIdx.x;
-  const int U = B * groups;
-  const int per = (U + 1023) / 1024;
-  const int u0 = tid * per < U ? tid * per : U;
-  const int u1 = u0 + per < U ? u0 + per : U;
-  auto tiles = [&](int u) {
-    const int L = seq_lens[u / groups];
-    return L > 0 ? (L + 31) >> 5 : 0;
-  };
-  int sum = 0;
-  for (int u = u0; u < u1; ++u) sum += tiles(u);
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = part[tid] - sum;
-  for (int u = u0; u < u1; ++u) {
-    prefix[u] = run;
-    run += tiles(u);
-  }
-  if (tid == 1023) prefix[U] = part[1023];
+// Uniform plan: partials [B, S, rows, Dc] / [B, S, rows]; one wavefront per
+// (request, row).
+__global__ void __launch_bounds__(256)
+mla_combine_kernel(int B, int S, int rows, int Dc, const float* __restrict__ po,
+                   const float* __restrict__ pl, int out_dtype, void* out, float* lse) {
+  const int wave = threadIdx.x >> 6;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + wave;
+  if (idx >= (int64_t)B * rows) return;
+  const int b = (int)(idx / rows), r = (int)(idx - (int64_t)b * rows);
+  merge_row(S, Dc, [&](int k) { return ((int64_t)b * S + k) * rows + r; }, po, pl, out_dtype, out,
+            idx, lse);
 }
 
+// ------------------------------------------------------- balanced merge
 // Merge for the balanced work list (same arithmetic as mla_combine_kernel).
 // With W tiles cut into nb = min(NB, W) ranges [k W / nb, (k+1) W / nb),
 // tile x lies in range ceil((x+1) nb / W) - 1.  A unit whose tiles [su, eu)
@@ -1049,36 +1116,12 @@ mla_combine_balanced_kernel(int B, int M, int Dc, int NB, const int32_t* __restr
   const int k2 = (int)((eu * nb + W - 1) / W - 1);
   if (k1 == k2) return;  // written by the split kernel
   const int ns = k2 - k1 + 1;
-  auto slot_row = [&](int j) -> int64_t {
-    const int64_t slot = j == 0 ? 2LL * k1 + 1 : 2LL * (k1 + j);
-    return slot * kBalancedRows + lr;
-  };
-  float mx = neg_inf();
-  for (int j = lane; j < ns; j += 64) mx = fmaxf(mx, pl[slot_row(j)]);
-  mx = wave_max(mx);
-  float wsum = 0.0f;
-  for (int j = lane; j < ns; j += 64) {
-    const float v = pl[slot_row(j)];
-    wsum += v == neg_inf() ? 0.0f : fast_exp2((v - mx) * kLog2e);
-  }
-  wsum = wave_sum(wsum);
-  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  for (int d = 4 * lane; d < Dc; d += 256) {
-    floatx4 a = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j = 0; j < ns; ++j) {
-      const int64_t pr = slot_row(j);
-      const float v = pl[pr];
-      if (v == neg_inf()) continue;
-      const float w = fast_exp2((v - mx) * kLog2e);
-      a += w * *(const floatx4*)(po + pr * Dc + d);
-    }
-    a *= inv;
-    if (out_dtype == kBF16)
-      *(bf16x4*)((__bf16*)out + ob + d) = bf16x4{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]};
-    else
-      *(floatx4*)((float*)out + ob + d) = a;
-  }
-  if (lse && lane == 0) lse[idx] = wsum > 0.0f ? mx + __logf(wsum) : neg_inf();
+  merge_row(ns, Dc,
+            [&](int j) -> int64_t {
+              const int64_t slot = j == 0 ? 2LL * k1 + 1 : 2LL * (k1 + j);
+              return slot * kBalancedRows + lr;
+            },
+            po, pl, out_dtype, out, idx, lse);
 }
 
 // ------------------------------------------------------------ gather hook
@@ -1105,7 +1148,8 @@ hipError_t launch_mfma(const SplitParams& p, hipStream_t stream) {
   static_assert(kRows == kBalancedRows, "balanced units are one workgroup of rows");
   const int units = p.B * p.S;
   const int64_t blocks = p.NB > 0 ? p.NB : 8LL * groups * ((units + 7) / 8);
-  const size_t lds = (size_t)STAGES * Tile<FP8>::kStage + 8 * WAVES;  // + restart requests
+  // + restart requests + plan scratch
+  const size_t lds = (size_t)STAGES * Tile<FP8>::kStage + 8 * WAVES + 4 * (WAVES + 2);
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
@@ -1152,12 +1196,6 @@ hipError_t launch_combine(int32_t B, int32_t S, int32_t rows, int32_t Dc, const 
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream, B, S,
                      rows, Dc, part_o, part_lse, out_dtype, out, lse);
-  return hipGetLastError();
-}
-
-hipError_t launch_plan(int32_t B, int32_t groups, const int32_t* seq_lens, int32_t* tile_prefix,
-                       hipStream_t stream) {
-  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, stream, B, groups, seq_lens, tile_prefix);
   return hipGetLastError();
 }
 

@@ -144,6 +144,44 @@ def test_balanced_work_list(mla, monkeypatch, name, plan):
         assert (out[4] == 0).all() and np.isneginf(lse[4]).all()
 
 
+@pytest.mark.parametrize("nw", [1, 3, 0])
+def test_balanced_stages(mla, nw):
+    """The two balanced stages called directly, with few workgroups (each takes
+    many segments) and with the device's own count (0): the tile prefix is
+    exact, the output matches the oracle, and with the device's count it is
+    bitwise the output of mla_decode."""
+    w = BALANCED_CASES["mixed"]
+    inp = synth.make_inputs(w)
+    dev = to_device(inp)
+    pr = mla.make_problem(dev["q_abs"], dev["q_rope"], dev["kv"], dev["page_table"],
+                          causal=w.causal, max_seq_len=w.max_seq_len)
+    nwk = nw or mla.balanced_workgroups()
+    groups = -(-w.rows // mla.BALANCED_ROWS)
+    prefix = torch.full((w.batch * groups + 1,), -7, dtype=torch.int32, device="cuda")
+    out = torch.empty((w.batch, w.q_len, w.heads, w.d_latent), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.batch, w.q_len, w.heads), dtype=torch.float32, device="cuda")
+    slot_o = torch.full((2 * nwk, mla.BALANCED_ROWS, w.d_latent), float("nan"), device="cuda")
+    slot_l = torch.full((2 * nwk, mla.BALANCED_ROWS), float("nan"), device="cuda")
+    mla.decode_split_balanced(pr, dev["q_abs"], dev["q_rope"], dev["kv"], dev["page_table"],
+                              dev["seq_lens"], float(inp["scale"]), nwk, prefix, out, lse,
+                              slot_o, slot_l, kv_scales=dev["kv_scales"])
+    mla.combine_balanced(pr, nwk, prefix, slot_o, slot_l, out, lse)
+    torch.cuda.synchronize()
+    L = inp["seq_lens"].astype(np.int64)
+    tiles = np.repeat((np.maximum(L, 0) + 31) // 32, groups)
+    expect = np.concatenate([[0], np.cumsum(tiles)])
+    assert np.array_equal(prefix.cpu().numpy(), expect)
+    o, l = out.double().cpu().numpy(), lse.double().cpu().numpy()
+    ro, rl = oracle.attend(inp)
+    assert_close(o, ro, tolerance(w), f"stages nw={nwk}")
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(l), fin)
+    assert np.abs(l[fin] - rl[fin]).max() <= 1e-3 * max(1.0, np.abs(rl[fin]).max())
+    if nw == 0:
+        o2, l2 = run_decode(mla, inp)
+        assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
 # -------------------------------------------------------- bit-exact indexing
 
 @pytest.mark.parametrize("index", [0, 1, 4])
