@@ -492,9 +492,10 @@ mla_split_mfma(SplitParams p, int groups) {
     wsu = eu;
     more_segments = wx < wx1;
   }
-  // the previous segment's waves are done with every stage before this one
-  // refills them
+  // the previous segment's waves are done with every stage (and with the
+  // restart words, cleared here) before this one refills them
   __syncthreads();
+  if (tid < 2) ((volatile LDS_AS uint32_t*)(smem + STAGES * G::kStage))[tid] = 0;
 
   const int lr = 32 * wave + n;  // this lane's row within the group
   const int gr = g * kRows + lr;  // this lane's query row
@@ -503,22 +504,44 @@ mla_split_mfma(SplitParams p, int groups) {
   const int vis = p.causal ? (L - p.T + 1 + t) : L;
   const int lim = vis < ce ? vis : ce;  // tokens >= lim are masked for this row
 
-  // ---- query fragments (B operand).  Padding rows (gr >= M) reuse row
-  // M - 1: they are computed like any row and never written out.
+  // ---- query fragments (B operand), staged through LDS: each wave copies
+  // its 32 rows into its own region of the idle stages with whole-row
+  // direct-to-LDS loads (one 1 KB latent row per load, eight 128-byte rope
+  // rows per load) and reads its fragments from there; loaded straight into
+  // the fragment layout, every load would touch 32 rows.  Padding rows
+  // (gr >= M) reuse row M - 1: they are computed like any row and never
+  // written out.
   bf16x8 qf[36];
   {
-    const int64_t qrow = (int64_t)b * M + (row_ok ? gr : M - 1);
-    const __bf16* qa = (const __bf16*)p.q_abs + qrow * 512;
-    const __bf16* qr = (const __bf16*)p.q_rope + qrow * 64;
+    constexpr int kQPitch = 1024 + 16;  // latent row pitch (conflict-free fragment reads)
+    constexpr int kQWave = 32 * kQPitch + 32 * 128;
+    static_assert(WAVES * kQWave <= STAGES * G::kStage, "query staging fits the stages");
+    LDS_AS char* qst = smem + wave * kQWave;
+    LDS_AS char* qrs = qst + 32 * kQPitch;
+    const int64_t qrow0 = (int64_t)b * M;
+    const int wr0 = g * kRows + 32 * wave;
+    const int ql = fresh_lane();
+#pragma unroll 4
+    for (int r = 0; r < 32; ++r) {
+      const int rr = wr0 + r < M ? wr0 + r : M - 1;
+      lds_dma16((const char*)p.q_abs + (qrow0 + rr) * 1024, 16 * ql, lds_addr(qst + r * kQPitch));
+    }
 #pragma unroll
-    for (int kk = 0; kk < 32; ++kk) qf[kk] = *(const bf16x8*)(qa + qfrag_dim<FP8>(kk, h));
+    for (int j = 0; j < 4; ++j) {
+      const int rb = wr0 + 8 * j < M ? wr0 + 8 * j : M - 1;
+      const int rl = wr0 + 8 * j + (ql >> 3) < M ? wr0 + 8 * j + (ql >> 3) : M - 1;
+      lds_dma16((const char*)p.q_rope + (qrow0 + rb) * 128, (rl - rb) * 128 + 16 * (ql & 7),
+                lds_addr(qrs + 1024 * j));
+    }
+    wait_vmcnt<0>();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = *(const bf16x8*)(qr + qfrag_dim<FP8>(kk, h));
+    for (int kk = 0; kk < 32; ++kk)
+      qf[kk] = *(const LDS_AS bf16x8*)(qst + n * kQPitch + 2 * qfrag_dim<FP8>(kk, h));
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qf[32 + kk] = *(const LDS_AS bf16x8*)(qrs + n * 128 + 2 * qfrag_dim<FP8>(kk, h));
+    __syncthreads();  // every wave has its fragments before the stages refill
   }
-  // Settle the query loads here, once: otherwise the compiler guards their
-  // first use inside the tile loop with vector-memory waits that would also
-  // wait for every tile prefetch in flight.
-  wait_vmcnt<0>();
 
   floatx16 acc[16];
 #pragma unroll
@@ -566,6 +589,17 @@ mla_split_mfma(SplitParams p, int groups) {
     const float* sg;
     LDS_AS char* dst;
   };
+  // The kLoads direct-to-LDS loads of a later tile are spread over the
+  // whole step, the first kQkLoads between the score MFMAs (one every
+  // kQkEvery steps of the score loop) and the rest between the value MFMAs
+  // (one every kPvEvery), so that the CU's load issue never bursts.
+  constexpr int kQkSteps = FP8 ? 18 : 36;
+  // (FP8 tiles are half the bytes and stay in the score loop)
+  constexpr int kQkLoads = FP8 ? kLoads : (kLoads * 36 + 67) / 68;
+  constexpr int kPvLoads = kLoads - kQkLoads;
+  constexpr int kQkEvery = kQkSteps / kQkLoads;
+  constexpr int kPvEvery = kPvLoads > 0 ? 32 / kPvLoads : 33;
+  static_assert(kQkEvery * kQkLoads <= kQkSteps && kPvEvery * kPvLoads <= 32, "load spread");
   auto scores = [&](LDS_AS char* st, floatx16& sacc, const Loader& ld, auto with_loads) {
     constexpr bool kLd = decltype(with_loads)::value;
     floatx16 s0;
@@ -585,8 +619,8 @@ mla_split_mfma(SplitParams p, int groups) {
       for (int kk = 0; kk < 36; ++kk) {
         const bf16x8 a = ring[kk % kAhead];
         if (kk + kAhead < 36) ring[kk % kAhead] = *kaddr(kk + kAhead);
-        if (kLd && (kk & 3) == 2 && (kk >> 2) < kLoads)
-          issue_piece<FP8, WAVES>(ld.tg, ld.sg, ld.dst, wave, lane, kk >> 2);
+        if (kLd && kk % kQkEvery == kQkEvery - 1 && kk / kQkEvery < kQkLoads)
+          issue_piece<FP8, WAVES>(ld.tg, ld.sg, ld.dst, wave, lane, kk / kQkEvery);
         if (kk == 0) mfma_v0(s0, a, qf[0]);
         else if (kk < 35) mfma_v(s0, a, qf[kk]);
         else mfma_v_last(s0, a, qf[kk]);
@@ -605,8 +639,8 @@ mla_split_mfma(SplitParams p, int groups) {
       for (int kk = 0; kk < 18; ++kk) {
         const uintx4 raw = ring[kk % kAhead];
         if (kk + kAhead < 18) ring[kk % kAhead] = *kaddr(kk + kAhead);
-        if (kLd && kk % 3 == 1 && kk / 3 < kLoads)
-          issue_piece<FP8, WAVES>(ld.tg, ld.sg, ld.dst, wave, lane, kk / 3);
+        if (kLd && kk % kQkEvery == 1 && kk / kQkEvery < kQkLoads)
+          issue_piece<FP8, WAVES>(ld.tg, ld.sg, ld.dst, wave, lane, kk / kQkEvery);
         const int q0 = kk < 16 ? 2 * kk : 32 + 2 * (kk - 16);
         const bf16x8 a0 = e4m3x8_to_bf16(raw[0], raw[1]);
         const bf16x8 a1 = e4m3x8_to_bf16(raw[2], raw[3]);
@@ -619,15 +653,15 @@ mla_split_mfma(SplitParams p, int groups) {
     sacc = s0;
   };
 
-  // Restart requests: word [i % 2][wave] is written by every wave while it
+  // Restart requests: byte [i % 2][wave] is written by every wave while it
   // handles tile i and read by all waves after the barrier that opens tile
-  // i + 1; it is next written for tile i + 2, after the following barrier.
-  volatile LDS_AS int* req = (volatile LDS_AS int*)(smem + STAGES * G::kStage);
+  // i + 1 (the four bytes of a tile in one 32-bit read, which the barrier
+  // orders after the writes); it is next written for tile i + 2, after the
+  // following barrier.  Both words are cleared before step 0.
+  static_assert(WAVES == 4, "one byte per wave in a 32-bit restart word");
+  volatile LDS_AS uint8_t* req = (volatile LDS_AS uint8_t*)(smem + STAGES * G::kStage);
   auto restart_word = [&](int i) -> int {
-    int any = 0;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) any |= req[(i & 1) * WAVES + w];
-    return any;
+    return (int)*(const LDS_AS uint32_t*)(smem + STAGES * G::kStage + 4 * (i & 1));
   };
 
   // One step of the softmax of tile i (32 steps per tile, interleaved with the
@@ -703,7 +737,11 @@ mla_split_mfma(SplitParams p, int groups) {
   // of tile i after each MFMA (each step is its own scheduling region, so the
   // VALU work sits between the MFMAs instead of after them).
   auto values_softmax = [&](LDS_AS char* sv, const bf16x8 (&pw)[2], LDS_AS char* st, int i,
-                            floatx16& z, bf16x8 (&pb)[2]) {
+                            floatx16& z, bf16x8 (&pb)[2], const Loader& ld, bool with_loads) {
+    auto pv_load = [&](int x2) {
+      if (kPvLoads > 0 && x2 % kPvEvery == kPvEvery - 1 && x2 / kPvEvery < kPvLoads && with_loads)
+        issue_piece<FP8, WAVES>(ld.tg, ld.sg, ld.dst, wave, lane, kQkLoads + x2 / kPvEvery);
+    };
     const int lim_rel = lim - (cb + 32 * i);
     SoftmaxState sm{neg_inf(), neg_inf(), 0.0f, false};
     // FP8: the scales of this lane's 16 tokens (two runs of 8), read up front
@@ -751,6 +789,7 @@ mla_split_mfma(SplitParams p, int groups) {
         if (x2 + kAhead < 32) ring[x2 % kAhead] = vread(x2 + kAhead);
         acc[x2 & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pw[x2 >> 4], acc[x2 & 15], 0, 0, 0);
         softmax_step(x2, tscv, lim_rel, z, pb, sm, i);
+        pv_load(x2);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -773,6 +812,7 @@ mla_split_mfma(SplitParams p, int groups) {
         acc[x2 & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             e4m3x8_to_bf16((unsigned)v[0], (unsigned)v[1]), pw[x2 >> 4], acc[x2 & 15], 0, 0, 0);
         softmax_step(x2, tscv, lim_rel, z, pb, sm, i);
+        pv_load(x2);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -801,7 +841,7 @@ mla_split_mfma(SplitParams p, int groups) {
       wait_ahead<kLoads>(ahead_tiles < 0 ? 0 : (ahead_tiles < kDepth - 1 ? ahead_tiles : kDepth - 1));
       __syncthreads();
       // restart requests of tile i - 1: read now, acted on after the scores
-      const int asked = i >= 1 ? restart_word(i - 1) : 0;
+      const int asked = restart_word(i - 1);  // zero for i = 0 (cleared per segment)
       // tile i + kDepth goes to the stage freed by tile i - 2
       const int64_t row0 = row_of(i + kDepth, pg_next);
       const Loader ld{kv + row0 * G::kRowBytes, FP8 ? p.kv_scales + row0 : nullptr,
@@ -826,7 +866,7 @@ mla_split_mfma(SplitParams p, int groups) {
       }
       __builtin_amdgcn_sched_barrier(0);
       bf16x8 pcur[2];
-      values_softmax(stage_of(i + STAGES - 1), pprev, st, i, z, pcur);
+      values_softmax(stage_of(i + STAGES - 1), pprev, st, i, z, pcur, ld, i + kDepth < ntiles);
       pprev[0] = pcur[0];
       pprev[1] = pcur[1];
       // branch-free: past the last tile this re-reads a valid entry and is unused
@@ -834,9 +874,11 @@ mla_split_mfma(SplitParams p, int groups) {
                              (i + kDepth + 1 < ntiles ? (cb + 32 * (i + kDepth + 1)) / p.P : 0));
     }
     if (!restart) break;
-    // Rare path: drain the pipeline, reset, and run the chunk again.
+    // Rare path: drain the pipeline, reset, and run the chunk again (the
+    // restart words are cleared too: step 0 reads them).
     wait_vmcnt<0>();
     __syncthreads();
+    if (tid < 2) ((volatile LDS_AS uint32_t*)(smem + STAGES * G::kStage))[tid] = 0;
     clear_stage(stage_of(STAGES - 1));
     m_ref = m_seen;
     l_part = 0.0f;
@@ -855,32 +897,61 @@ mla_split_mfma(SplitParams p, int groups) {
   const float l_tot = half_swap_sum(l_part + l_part2);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_v = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : neg_inf();
-  // one straight store sequence per destination kind: normalised rows of
-  // out (bf16 or fp32) for a whole unit, fp32 partial rows otherwise
-  auto store_rows = [&](auto* dst, auto cvt) {
-#pragma unroll
-    for (int db = 0; db < 16; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *(decltype(cvt(floatx4{}))*)(dst + 32 * db + 8 * g4 + 4 * h) =
-            cvt(floatx4{acc[db][4 * g4 + 0] * inv, acc[db][4 * g4 + 1] * inv,
-                        acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv});
-  };
-  auto to_bf16 = [](floatx4 v) { return bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]}; };
-  auto to_f32 = [](floatx4 v) { return v; };
+  // The rows go out through LDS: each wave writes its normalised rows into
+  // its own region of the (now idle) stages, row r at r * kPitch, then reads
+  // them back a row at a time, so that every store writes 1 KB of one row.
+  // Stored straight from the accumulator layout, one instruction would write
+  // 32 bytes into each of 32 rows (32 partial cache lines).  fp32 rows go in
+  // two passes of 256 columns, bf16 rows in one.  The 16-byte pad keeps the
+  // row-scattered writes free of bank conflicts.
+  constexpr int kPitch = 1024 + 16;
+  static_assert(WAVES * 32 * kPitch <= STAGES * G::kStage, "output staging fits the stages");
   // (the destination row is taken through an empty asm statement so that
   // no address of it is computed before, and kept live through, the loop)
   asm volatile("" : "+s"(drow));
-  const int64_t orow = drow + lr;
-  if (row_ok) {
-    if (final_out) {
-      if (p.out_dtype == kBF16) store_rows((__bf16*)p.out + orow * 512, to_bf16);
-      else store_rows((float*)p.out + orow * 512, to_f32);
-      if (p.lse && h == 0) p.lse[orow] = lse_v;
-    } else {
-      store_rows(p.part_o + orow * 512, to_f32);
-      if (h == 0) p.part_lse[orow] = lse_v;
+  __syncthreads();  // every wave is done with the stages
+  LDS_AS char* wst = smem + wave * 32 * kPitch;
+  const int wrow0 = g * kRows + 32 * wave;  // query row of this wave's staged row 0
+  auto stage_out = [&](int db0, int ndb, auto cvt) {
+    constexpr int esz = sizeof(decltype(cvt(floatx4{}))) / 4;
+#pragma unroll
+    for (int db = 0; db < ndb; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const floatx4 v = floatx4{acc[db0 + db][4 * g4 + 0], acc[db0 + db][4 * g4 + 1],
+                                  acc[db0 + db][4 * g4 + 2], acc[db0 + db][4 * g4 + 3]} * inv;
+        *(decltype(cvt(v))*)(wst + n * kPitch + esz * (32 * db + 8 * g4 + 4 * h)) = cvt(v);
+      }
+  };
+  auto drain = [&](char* dst, int64_t row_bytes) {  // dst: this wave's row 0 at this pass's column
+#pragma unroll 1
+    for (int r0 = 0; r0 < 32; r0 += 8) {  // eight rows in flight at a time
+      uintx4 v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = *(const LDS_AS uintx4*)(wst + (r0 + r) * kPitch + 16 * lane);
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (wrow0 + r0 + r < M) *(uintx4*)(dst + (r0 + r) * row_bytes + 16 * lane) = v[r];
     }
+  };
+  auto to_bf16 = [](floatx4 v) { return bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]}; };
+  auto to_f32 = [](floatx4 v) { return v; };
+  const int64_t orow0 = drow + 32 * wave;
+  if (final_out && p.out_dtype == kBF16) {
+    stage_out(0, 16, to_bf16);
+    drain((char*)((__bf16*)p.out + orow0 * 512), 1024);
+  } else {
+    float* base = final_out ? (float*)p.out + orow0 * 512 : p.part_o + orow0 * 512;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      stage_out(8 * pass, 8, to_f32);
+      drain((char*)(base + 256 * pass), 2048);
+    }
+  }
+  if (row_ok && h == 0) {
+    const int64_t orow = drow + lr;
+    if (!final_out) p.part_lse[orow] = lse_v;
+    else if (p.lse) p.lse[orow] = lse_v;
   }
   }  // segments
 }
