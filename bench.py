@@ -264,7 +264,7 @@ def main():
         nw = mla.balanced_workgroups()
         groups = -(-R // mla.BALANCED_ROWS)
         prefix = torch.empty(B * groups + 1, dtype=torch.int32, device="cuda")
-        slot_o = torch.empty((2 * nw, mla.BALANCED_ROWS, Dc), dtype=torch.float32, device="cuda")
+        slot_o = torch.empty((2 * nw, mla.BALANCED_ROWS, Dc), dtype=torch.bfloat16, device="cuda")
         slot_l = torch.empty((2 * nw, mla.BALANCED_ROWS), dtype=torch.float32, device="cuda")
         bsplit_args = [(ctypes.byref(prs), P(d["q_abs"]), P(d["q_rope"]), P(d["kv"]),
                         P(d["kv_scales"]), P(d["page_table"]), P(d["seq_lens"]),

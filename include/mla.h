@@ -193,11 +193,11 @@ int mla_balanced_workgroups(int32_t* num_workgroups);
  * mla_decode().  Writes tile_prefix [U + 1] int32 (tile_prefix[u] = tiles of
  * the units before u, tile_prefix[U] = W) for the merge stage.  A segment
  * that is a whole unit writes its rows of out [B, T, H, Dc] (out_dtype) and
- * lse (if not NULL) directly.  Any other segment writes its normalised fp32
- * partial and natural-log lse to a slot: slot 2k if it continues a unit
- * begun in an earlier workgroup, 2k + 1 if it starts a unit that continues
- * in later ones, with
- *   slot_o   [2 * num_workgroups, 128, Dc] fp32 (row = unit row r - 128 g)
+ * lse (if not NULL) directly.  Any other segment writes its normalised
+ * partial, rounded to bf16, and its natural-log lse (fp32) to a slot: slot 2k
+ * if it continues a unit begun in an earlier workgroup, 2k + 1 if it starts a
+ * unit that continues in later ones, with
+ *   slot_o   [2 * num_workgroups, 128, Dc] bf16 (row = unit row r - 128 g)
  *   slot_lse [2 * num_workgroups, 128] fp32
  * Slots and out rows that no segment writes are left untouched.
  */
@@ -205,7 +205,7 @@ int mla_decode_split_balanced(const mla_problem* problem, const void* q_absorbed
                               const void* q_rope, const void* kv_pages, const float* kv_scales,
                               const int32_t* page_table, const int32_t* seq_lens, float scale,
                               int32_t num_workgroups, int32_t* tile_prefix, void* out,
-                              float* lse, float* slot_o, float* slot_lse, hipStream_t stream);
+                              float* lse, void* slot_o, float* slot_lse, hipStream_t stream);
 
 /*
  * Merge stage of the balanced work list, after mla_decode_split_balanced()
@@ -215,7 +215,7 @@ int mla_decode_split_balanced(const mla_problem* problem, const void* q_absorbed
  * units' rows are left as the split stage wrote them.
  */
 int mla_combine_balanced(const mla_problem* problem, int32_t num_workgroups,
-                         const int32_t* tile_prefix, const float* slot_o, const float* slot_lse,
+                         const int32_t* tile_prefix, const void* slot_o, const float* slot_lse,
                          void* out, float* lse, hipStream_t stream);
 
 /*

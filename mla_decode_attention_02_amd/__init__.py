@@ -227,7 +227,7 @@ def decode_split_balanced(problem, q_abs, q_rope, kv_pages, page_table, seq_lens
                           num_workgroups, tile_prefix, out, lse, slot_o, slot_lse, *,
                           kv_scales=None):
     """Split stage of the balanced work list: writes tile_prefix [U + 1], whole units
-    to out/lse and other segments to slot_o [2 nw, 128, Dc] / slot_lse [2 nw, 128]."""
+    to out/lse and other segments to slot_o [2 nw, 128, Dc] bf16 / slot_lse [2 nw, 128] fp32."""
     _validate(q_abs, q_rope, kv_pages, page_table, seq_lens, kv_scales)
     dev = q_abs.device
     nw = int(num_workgroups)
@@ -237,7 +237,7 @@ def decode_split_balanced(problem, q_abs, q_rope, kv_pages, page_table, seq_lens
         raise ValueError("tile_prefix too small")
     _require(out, "out", dev, dtype=_torch_dtype(problem.out_dtype))
     _require(lse, "lse", dev, dtype=torch.float32)
-    _require(slot_o, "slot_o", dev, dtype=torch.float32)
+    _require(slot_o, "slot_o", dev, dtype=torch.bfloat16)
     _require(slot_lse, "slot_lse", dev, dtype=torch.float32)
     if (slot_o.numel() < 2 * nw * BALANCED_ROWS * problem.d_latent
             or slot_lse.numel() < 2 * nw * BALANCED_ROWS):

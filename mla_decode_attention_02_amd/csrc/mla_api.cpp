@@ -126,7 +126,7 @@ BalancedLayout balanced_layout(const mla_problem* pr, int32_t NB) {
   l.prefix_off = 0;
   l.lse_off = up((units + 1) * sizeof(int32_t));
   l.o_off = l.lse_off + up(slot_rows * sizeof(float));
-  l.total = l.o_off + slot_rows * (size_t)pr->d_latent * sizeof(float);
+  l.total = l.o_off + slot_rows * (size_t)pr->d_latent * sizeof(uint16_t);  // bf16 slot rows
   return l;
 }
 
@@ -317,7 +317,7 @@ int mla_decode_split_balanced(const mla_problem* problem, const void* q_absorbed
                               const void* q_rope, const void* kv_pages, const float* kv_scales,
                               const int32_t* page_table, const int32_t* seq_lens, float scale,
                               int32_t num_workgroups, int32_t* tile_prefix, void* out,
-                              float* lse, float* slot_o, float* slot_lse, hipStream_t stream) {
+                              float* lse, void* slot_o, float* slot_lse, hipStream_t stream) {
   int rc = validate_problem(problem);
   if (rc) return rc;
   rc = validate_inputs(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table, seq_lens);
@@ -335,13 +335,13 @@ int mla_decode_split_balanced(const mla_problem* problem, const void* q_absorbed
   p.write_final = false;
   p.out = out;
   p.lse = lse;
-  p.part_o = slot_o;
+  p.part_o = (float*)slot_o;  // bf16 slot rows in balanced mode
   p.part_lse = slot_lse;
   return mla::launch_split(p, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 int mla_combine_balanced(const mla_problem* problem, int32_t num_workgroups,
-                         const int32_t* tile_prefix, const float* slot_o, const float* slot_lse,
+                         const int32_t* tile_prefix, const void* slot_o, const float* slot_lse,
                          void* out, float* lse, hipStream_t stream) {
   const int rc = validate_problem(problem);
   if (rc) return rc;

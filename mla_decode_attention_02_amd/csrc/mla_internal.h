@@ -24,7 +24,8 @@ struct SplitParams {
   bool write_final;            // S == 1: write out/lse directly
   void* out;                   // [B, T*H, Dc] out_dtype (write_final)
   float* lse;                  // [B, T*H] or nullptr (write_final)
-  float* part_o;               // [B, S, T*H, Dc] fp32 (!write_final)
+  float* part_o;               // uniform: [B, S, T*H, Dc] fp32 (!write_final);
+                               // balanced: slot rows [2 NB, 128, Dc] bf16
   float* part_lse;             // [B, S, T*H] fp32 (!write_final)
   bool force_generic;          // run the VALU kernel even where the MFMA one applies
   // Balanced work list (MFMA kernels only; NB == 0 selects uniform chunks):
@@ -47,7 +48,7 @@ inline int64_t balanced_units(int32_t B, int32_t T, int32_t H) {
 // workgroups, merge its partial slots into out/lse; units without tiles get
 // out = 0, lse = -inf; the others were written by the split kernel.
 hipError_t launch_combine_balanced(int32_t B, int32_t M, int32_t Dc, int32_t NB,
-                                   const int32_t* tile_prefix, const float* part_o,
+                                   const int32_t* tile_prefix, const void* part_o,
                                    const float* part_lse, int32_t out_dtype, void* out, float* lse,
                                    hipStream_t stream);
 

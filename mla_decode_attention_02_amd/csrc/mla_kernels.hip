@@ -940,6 +940,9 @@ mla_split_mfma(SplitParams p, int groups) {
   if (final_out && p.out_dtype == kBF16) {
     stage_out(0, 16, to_bf16);
     drain((char*)((__bf16*)p.out + orow0 * 512), 1024);
+  } else if (!final_out && p.NB > 0) {  // balanced slots hold bf16 partials
+    stage_out(0, 16, to_bf16);
+    drain((char*)((__bf16*)p.part_o + orow0 * 512), 1024);
   } else {
     float* base = final_out ? (float*)p.out + orow0 * 512 : p.part_o + orow0 * 512;
 #pragma unroll
@@ -1061,8 +1064,14 @@ __global__ void __launch_bounds__(256) mla_split_generic(SplitParams p) {
 // included); with none left, out = 0 and lse = -inf.  The normalised weights of 64 partials
 // at a time sit one per lane and are broadcast by shuffles, and each lane
 // accumulates 8 columns, so several partial rows are in flight per wave.
-template <typename SlotRow>
-__device__ __forceinline__ void merge_row(int ns, int Dc, SlotRow slot_row, const float* __restrict__ po,
+__device__ __forceinline__ floatx4 load4(const float* p) { return *(const floatx4*)p; }
+__device__ __forceinline__ floatx4 load4(const __bf16* p) {
+  const bf16x4 v = *(const bf16x4*)p;
+  return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+template <typename PT, typename SlotRow>
+__device__ __forceinline__ void merge_row(int ns, int Dc, SlotRow slot_row, const PT* __restrict__ po,
                                           const float* __restrict__ pl, int out_dtype, void* out,
                                           int64_t out_row, float* lse) {
   const int lane = threadIdx.x & 63;
@@ -1106,9 +1115,9 @@ __device__ __forceinline__ void merge_row(int ns, int Dc, SlotRow slot_row, cons
           for (int q = 0; q < 4; ++q) {
             const int j = jj + q < cnt ? jj + q : cnt - 1;
             w[q] = jj + q < cnt ? __shfl(wj, j, 64) : 0.0f;
-            const float* row = po + slot_row(j0 + j) * Dc;
-            x[q] = oka ? *(const floatx4*)(row + da) : floatx4{};
-            y[q] = okb ? *(const floatx4*)(row + db) : floatx4{};
+            const PT* row = po + slot_row(j0 + j) * Dc;
+            x[q] = oka ? load4(row + da) : floatx4{};
+            y[q] = okb ? load4(row + db) : floatx4{};
           }
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -1130,7 +1139,7 @@ __device__ __forceinline__ void merge_row(int ns, int Dc, SlotRow slot_row, cons
       for (int j = 0; j < ns; ++j) {
         const float v = pl[slot_row(j)];
         if (v == neg_inf()) continue;
-        a += fast_exp2((v - mx) * kLog2e) * inv * po[slot_row(j) * Dc + d];
+        a += fast_exp2((v - mx) * kLog2e) * inv * (float)po[slot_row(j) * Dc + d];
       }
       if (out_dtype == kBF16) ((__bf16*)out)[ob + d] = (__bf16)a;
       else ((float*)out)[ob + d] = a;
@@ -1161,7 +1170,7 @@ mla_combine_kernel(int B, int S, int rows, int Dc, const float* __restrict__ po,
 // wave per output row.
 __global__ void __launch_bounds__(256)
 mla_combine_balanced_kernel(int B, int M, int Dc, int NB, const int32_t* __restrict__ prefix,
-                            const float* __restrict__ po, const float* __restrict__ pl,
+                            const __bf16* __restrict__ po, const float* __restrict__ pl,
                             int out_dtype, void* out, float* lse) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t idx = (int64_t)blockIdx.x * 4 + wave;
@@ -1271,13 +1280,13 @@ hipError_t launch_combine(int32_t B, int32_t S, int32_t rows, int32_t Dc, const 
 }
 
 hipError_t launch_combine_balanced(int32_t B, int32_t M, int32_t Dc, int32_t NB,
-                                   const int32_t* tile_prefix, const float* part_o,
+                                   const int32_t* tile_prefix, const void* part_o,
                                    const float* part_lse, int32_t out_dtype, void* out, float* lse,
                                    hipStream_t stream) {
   const int64_t n = (int64_t)B * M;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(mla_combine_balanced_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream,
-                     B, M, Dc, NB, tile_prefix, part_o, part_lse, out_dtype, out, lse);
+                     B, M, Dc, NB, tile_prefix, (const __bf16*)part_o, part_lse, out_dtype, out, lse);
   return hipGetLastError();
 }
 

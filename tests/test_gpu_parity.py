@@ -160,7 +160,8 @@ def test_balanced_stages(mla, nw):
     prefix = torch.full((w.batch * groups + 1,), -7, dtype=torch.int32, device="cuda")
     out = torch.empty((w.batch, w.q_len, w.heads, w.d_latent), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.batch, w.q_len, w.heads), dtype=torch.float32, device="cuda")
-    slot_o = torch.full((2 * nwk, mla.BALANCED_ROWS, w.d_latent), float("nan"), device="cuda")
+    slot_o = torch.full((2 * nwk, mla.BALANCED_ROWS, w.d_latent), float("nan"), dtype=torch.bfloat16,
+                        device="cuda")
     slot_l = torch.full((2 * nwk, mla.BALANCED_ROWS), float("nan"), device="cuda")
     mla.decode_split_balanced(pr, dev["q_abs"], dev["q_rope"], dev["kv"], dev["page_table"],
                               dev["seq_lens"], float(inp["scale"]), nwk, prefix, out, lse,
@@ -227,7 +228,7 @@ def _one_hot_inputs(w, seed, positions):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-@pytest.mark.parametrize("S", [1, 3])
+@pytest.mark.parametrize("S", [1, 3, 0])
 def test_one_hot_probe_returns_the_selected_row(mla, kv, S):
     base = 1 if kv == "bf16" else 4
     w = small(base, batch=3, heads=64, seq_lens=("fixed", (40, 333, 1000)), decoys=2, index=40)
