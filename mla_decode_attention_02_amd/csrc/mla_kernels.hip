@@ -779,7 +779,7 @@ mla_split_mfma(SplitParams p, int groups) {
         const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(b0 + 16 * 273));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      constexpr int kAhead = 3;  // value operands in flight ahead of their MFMA
+      constexpr int kAhead = 5;  // value operands in flight ahead of their MFMA
       bf16x8 ring[kAhead];
 #pragma unroll
       for (int x2 = 0; x2 < kAhead; ++x2) ring[x2] = vread(x2);
