@@ -57,6 +57,12 @@ def load(rebuild=False):
     lib.orc_bf16_value.restype = ctypes.c_double
     lib.orc_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.orc_e4m3_value.restype = ctypes.c_double
+    lib.orc_append_rows.argtypes = [i32, i32, i32, P, P, i32, i32, i32, P, i32, P, P]
+    lib.orc_append_rows.restype = ctypes.c_int
+    lib.orc_e4m3_code.argtypes = [ctypes.c_float]
+    lib.orc_e4m3_code.restype = ctypes.c_uint8
+    lib.orc_bf16_bits.argtypes = [ctypes.c_float]
+    lib.orc_bf16_bits.restype = ctypes.c_uint16
     lib.orc_max_threads.argtypes = []
     lib.orc_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -184,3 +190,26 @@ def e4m3_value(code):
 
 def max_threads():
     return load().orc_max_threads()
+
+
+def append_rows(src, page_table, pos0, kv, kv_scales=None, dst="fp8"):
+    """Paged KV append (see orc_append_rows): src [n_req, T, D] float32 exact
+    source values; writes rows into kv [NP, P, D] (uint8 codes / uint16 bf16
+    bits / float32) and, for fp8, per-token scales into kv_scales [NP, P]."""
+    src = np.ascontiguousarray(src, dtype=np.float32)
+    n_req, T, D = src.shape
+    NP, P = kv.shape[0], kv.shape[1]
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    p0 = np.ascontiguousarray(pos0, dtype=np.int32)
+    assert kv.flags.c_contiguous and (kv_scales is None or kv_scales.flags.c_contiguous)
+    rc = load().orc_append_rows(n_req, T, D, _ptr(src), _ptr(pt), pt.shape[1], P, NP, _ptr(p0),
+                                _DT[dst], _ptr(kv), None if kv_scales is None else _ptr(kv_scales))
+    _check(rc, "orc_append_rows")
+
+
+def e4m3_code(q):
+    return int(load().orc_e4m3_code(float(q)))
+
+
+def bf16_bits(v):
+    return int(load().orc_bf16_bits(float(v)))

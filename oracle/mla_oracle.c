@@ -345,6 +345,96 @@ int orc_gather_rows(const orc_problem* pr, const void* kv, const int32_t* page_t
   return ORC_OK;
 }
 
+/*
+ * Paged KV append with FP8 packing (the write that produces the cache the
+ * decode reads).  Each new row is a token's Dc + Dr values; token t of
+ * request b lands at logical position pos0[b] + t, i.e. in page
+ * page_table[b][pos / P], slot pos mod P (PagedAttention article on the
+ * "推理优化" tag page), and is stored as
+ *   - fp32: the value itself;
+ *   - bf16: the value rounded to the nearest bf16, ties to even (the upper
+ *     half of binary32 after rounding; NaN stays NaN);
+ *   - E4M3: one fp32 scale per row, s = absmax / 448 computed in fp32 (448 =
+ *     largest finite E4M3, FP8 format table of the quantisation article on
+ *     the same tag page), s = 1 for an all-zero row; each value v becomes the
+ *     E4M3 code nearest to the fp32 quotient q = v / s (ties to even, |q| >
+ *     448 saturates to 448, the sign kept, so -0 gives the code of -0), and s
+ *     goes to scales[page][slot].
+ * The E4M3 code of q is found from the format's definition: below 2^-6 the
+ * values are multiples of 2^-9 (codes 0..7 per sign), from 2^e (e = -6..8)
+ * on the step is 2^(e-3); the code of a value is (e + 7) << 3 | mantissa.
+ * src: [n_req, T, D] fp32 holding the exact source values.
+ */
+static uint8_t e4m3_code_of(float q) {
+  if (isnan(q)) return 0x7F;
+  const uint8_t sign = signbit(q) ? 0x80 : 0x00;
+  const double a = fabs((double)q);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < ldexp(1.0, -6)) {  /* subnormal range: multiples of 2^-9 (code 8 = 2^-6) */
+    const double m = nearbyint(ldexp(a, 9)); /* exact scaling; ties to even */
+    return sign | (uint8_t)m;
+  }
+  int e;
+  frexp(a, &e);  /* a = f * 2^e, f in [0.5, 1): a in [2^(e-1), 2^e) */
+  e -= 1;        /* a in [2^e, 2^(e+1)) */
+  double m = nearbyint(ldexp(a, 3 - e)); /* 8 .. 16 */
+  if (m == 16.0) {
+    m = 8.0;
+    e += 1;
+  }
+  int code = ((e + 7) << 3) | ((int)m - 8);
+  if (code > 0x7E) code = 0x7E;
+  return sign | (uint8_t)code;
+}
+
+static uint16_t bf16_bits_of(float v) {
+  uint32_t u;
+  memcpy(&u, &v, 4);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);  /* NaN stays NaN */
+  const uint32_t lsb = (u >> 16) & 1u;
+  return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+int orc_append_rows(int32_t n_req, int32_t T, int32_t D, const float* src, const int32_t* page_table,
+                    int32_t MP, int32_t P, int32_t NP, const int32_t* pos0, int32_t dst_dtype, void* kv,
+                    float* scales) {
+  if (n_req < 0 || T < 1 || D < 1 || P < 1 || MP < 1 || NP < 1 || !src || !page_table || !pos0 || !kv)
+    return ORC_BAD_ARG;
+  if (dst_dtype != ORC_F32 && dst_dtype != ORC_BF16 && dst_dtype != ORC_E4M3) return ORC_BAD_ARG;
+  if (dst_dtype == ORC_E4M3 && !scales) return ORC_BAD_ARG;
+  for (int b = 0; b < n_req; ++b) {
+    for (int t = 0; t < T; ++t) {
+      const int64_t pos = (int64_t)pos0[b] + t;
+      if (pos < 0 || pos >= (int64_t)MP * P) return ORC_BAD_ARG;
+      const int32_t page = page_table[(size_t)b * MP + pos / P];
+      if (page < 0 || page >= NP) return ORC_BAD_PAGE;
+      const size_t row = (size_t)page * P + (size_t)(pos % P);
+      const float* x = src + ((size_t)b * T + t) * D;
+      if (dst_dtype == ORC_F32) {
+        memcpy((float*)kv + row * D, x, sizeof(float) * (size_t)D);
+      } else if (dst_dtype == ORC_BF16) {
+        uint16_t* o = (uint16_t*)kv + row * D;
+        for (int d = 0; d < D; ++d) o[d] = bf16_bits_of(x[d]);
+      } else {
+        float amax = 0.0f;
+        for (int d = 0; d < D; ++d) {
+          const float a = fabsf(x[d]);
+          if (a > amax) amax = a;
+        }
+        const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        uint8_t* o = (uint8_t*)kv + row * D;
+        for (int d = 0; d < D; ++d) o[d] = e4m3_code_of(x[d] / s);
+        scales[row] = s;
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* E4M3 code of one fp32 value (for pinning the encoder on its own). */
+uint8_t orc_e4m3_code(float q) { return e4m3_code_of(q); }
+uint16_t orc_bf16_bits(float v) { return bf16_bits_of(v); }
+
 int orc_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -447,3 +447,133 @@ def test_workload_rows_follow_the_pages():
         assert w.d_latent == facts["latent_row"]["d_latent"]
         assert w.d_rope == facts["latent_row"]["d_rope"]
     assert synth.WORKLOADS[0].page_size == facts["paged_block"]["example_block_size"]
+
+
+# ------------------------------------------------ paged KV append (FP8 pack)
+
+def _e4m3_all_finite():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    keep = np.isfinite(vals)
+    return codes[keep], vals[keep]
+
+
+def test_e4m3_encoder_against_torch_cast():
+    """The oracle's E4M3 encoder (from the format definition) against torch's
+    float8_e4m3fn cast, an independent implementation: every finite code, every
+    midpoint between neighbours (ties to even), one fp32 step either side of
+    each midpoint, and random values in range."""
+    codes, vals = _e4m3_all_finite()
+    pos = np.unique(np.abs(vals))
+    mids = (pos[:-1].astype(np.float64) + pos[1:]) / 2
+    probe = [vals.astype(np.float32)]
+    for m in mids:
+        f = np.float32(m)
+        probe.append(np.array([f, np.nextafter(f, np.float32(0)), np.nextafter(f, np.float32(1e9)),
+                               -f], dtype=np.float32))
+    rng = np.random.default_rng(5)
+    probe.append((rng.uniform(-448, 448, 4000)).astype(np.float32))
+    probe.append((rng.standard_normal(4000) * np.float32(0.02)).astype(np.float32))
+    x = np.concatenate(probe)
+    x = x[np.abs(x) <= 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_code(v) for v in x], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_encoder_saturates_at_the_pages_maximum():
+    fmt = json.load(open(os.path.join(GOLDEN, "page_facts.json")))["fp8_formats"]["e4m3"]
+    top = oracle.e4m3_code(fmt["max_finite"])
+    assert oracle.e4m3_value(top) == fmt["max_finite"]
+    for v in (448.5, 479.9, 480.0, 1e6, 3e38, float("inf")):
+        assert oracle.e4m3_code(v) == top and oracle.e4m3_code(-v) == top | 0x80
+    assert oracle.e4m3_code(float("nan")) & 0x7F == 0x7F
+
+
+def test_bf16_encoder_against_torch_cast():
+    rng = np.random.default_rng(6)
+    x = np.concatenate([rng.standard_normal(5000).astype(np.float32),
+                        rng.uniform(-1e30, 1e30, 500).astype(np.float32),
+                        np.array([0.0, -0.0, 1.0, 3.0, np.inf, -np.inf], dtype=np.float32)])
+    # exact ties: bf16 values plus half a bf16 step
+    b = torch.from_numpy(x[:1000]).to(torch.bfloat16).float().numpy()
+    x = np.concatenate([x, (b.view(np.uint32) | np.uint32(0x8000)).view(np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_bits(v) for v in x], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def _append_case(seed, n_req=3, T=2, D=80, P=16, MP=6, NP=24, dst="fp8"):
+    rng = np.random.default_rng(seed)
+    src = (rng.standard_normal((n_req, T, D)) * 0.5).astype(np.float32)
+    src[0, 0] = 0.0                      # all-zero row: scale 1, codes of +0
+    src[0, 1, :5] = [-0.0, 1e-30, -1e-30, 3.0, -3.0]
+    pt = rng.permutation(NP)[: n_req * MP].reshape(n_req, MP).astype(np.int32)
+    pos0 = np.array([0, 15, 2 * P + 7], dtype=np.int32)[:n_req]   # one append crosses a page
+    elt = {"fp8": np.uint8, "bf16": np.uint16, "f32": np.float32}[dst]
+    kv = np.full((NP, P, D), 0x5A if dst == "fp8" else 0x7FC0 if dst == "bf16" else np.nan, dtype=elt)
+    sc = np.full((NP, P), np.nan, dtype=np.float32) if dst == "fp8" else None
+    return src, pt, pos0, kv, sc
+
+
+@pytest.mark.parametrize("dst", ["fp8", "bf16", "f32"])
+def test_append_paged_equals_contiguous(dst):
+    """Appending through a permuted page table and through one contiguous page
+    per request store the same rows, read back by logical position with the
+    (separately pinned) page-table gather; untouched slots keep their poison."""
+    src, pt, pos0, kv, sc = _append_case(11, dst=dst)
+    fresh = kv.copy()
+    n_req, T, D = src.shape
+    P, MP = kv.shape[1], pt.shape[1]
+    oracle.append_rows(src, pt, pos0, kv, sc, dst=dst)
+    kvc = np.zeros((n_req, MP * P, D), dtype=kv.dtype)
+    scc = None if sc is None else np.zeros((n_req, MP * P), dtype=np.float32)
+    oracle.append_rows(src, np.arange(n_req, dtype=np.int32)[:, None], pos0, kvc, scc, dst=dst)
+    written = set()
+    for b in range(n_req):
+        for t in range(T):
+            pos = int(pos0[b]) + t
+            page, slot = pt[b, pos // P], pos % P
+            written.add((page, slot))
+            assert kv[page, slot].tobytes() == kvc[b, pos].tobytes()
+            if sc is not None:
+                assert sc[page, slot] == scc[b, pos]
+    untouched = [(p, s) for p in range(kv.shape[0]) for s in range(P) if (p, s) not in written]
+    for p, s in untouched:
+        assert kv[p, s].tobytes() == fresh[p, s].tobytes()
+
+
+def test_append_fp8_rows_meet_the_format_error_bound():
+    """Each stored value decodes (code x scale) to within half a step of E4M3
+    around the source: relative 2^-4 above 2^-6 s, absolute 2^-10 s below; the
+    row's largest magnitude lands on the largest finite code."""
+    src, pt, pos0, kv, sc = _append_case(12, n_req=3, T=4, D=576, P=16, MP=8, NP=30)
+    oracle.append_rows(src, pt, pos0, kv, sc, dst="fp8")
+    table = np.array([oracle.e4m3_value(c) for c in range(256)])
+    for b in range(src.shape[0]):
+        for t in range(src.shape[1]):
+            pos = int(pos0[b]) + t
+            page, slot = pt[b, pos // 16], pos % 16
+            s = float(sc[page, slot])
+            x = src[b, t].astype(np.float64)
+            amax = np.abs(x).max()
+            assert s == (np.float32(amax) / np.float32(448) if amax > 0 else 1.0)
+            dec = table[kv[page, slot]] * s
+            tol = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * s) * (1 + 1e-6)
+            assert np.all(np.abs(dec - x) <= tol)
+            if amax > 0:
+                assert kv[page, slot][np.argmax(np.abs(x))] & 0x7F == 0x7E
+
+
+def test_append_fp8_matches_generator_encoder():
+    """The generator's row quantiser (written separately, used to build the FP8
+    workload) and the oracle's append agree bit for bit."""
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((1, 40, 576)) * 0.5).astype(np.float32)
+    kv = np.zeros((3, 16, 576), dtype=np.uint8)
+    sc = np.zeros((3, 16), dtype=np.float32)
+    oracle.append_rows(x, np.array([[2, 0, 1]], dtype=np.int32), np.array([0], dtype=np.int32), kv, sc)
+    codes, scales = synth.formats.quantize_rows_e4m3(x[0])
+    order = [(2, s) for s in range(16)] + [(0, s) for s in range(16)] + [(1, s) for s in range(8)]
+    for t, (pg, sl) in enumerate(order):
+        assert np.array_equal(kv[pg, sl], codes[t]) and sc[pg, sl] == scales[t]
