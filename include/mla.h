@@ -219,6 +219,30 @@ int mla_combine_balanced(const mla_problem* problem, int32_t num_workgroups,
                          void* out, float* lse, hipStream_t stream);
 
 /*
+ * Paged KV append with packing: the write that fills the cache the decode
+ * reads.  problem->batch = B requests, problem->q_len = T new tokens each,
+ * rows of D = d_latent + d_rope values; page_size, num_pages,
+ * max_pages_per_seq and kv_dtype describe the cache (other fields unused).
+ *   rows       [B, T, D] src_dtype (F32 or BF16), device
+ *   positions  [B] int32: token t of request b goes to logical position
+ *              positions[b] + t, i.e. page page_table[b][pos / P], slot pos mod P
+ *              ("推理优化" tag page, PagedAttention article)
+ *   kv_pages   [NP, P, D] kv_dtype; kv_scales [NP, P] fp32 for FP8_E4M3 (else NULL)
+ * Stored as: F32 the value; BF16 the nearest bf16 (ties to even, NaN stays
+ * NaN); FP8_E4M3 one fp32 scale per row s = absmax / 448 computed in fp32
+ * (448 = largest finite E4M3, quantisation article's FP8 table on the same
+ * page; s = 1 for an all-zero row) and per value the E4M3 code nearest to
+ * the fp32 quotient v / s (ties to even, magnitudes past 448 saturate, the
+ * sign kept; NaN gives 0x7F).  Only the appended slots are written.
+ * Preconditions (not checked on the device): positions[b] + T <= MP * P and
+ * the page-table entries covering those positions are valid page ids; the
+ * appended slots of different requests are distinct.
+ */
+int mla_append_kv(const mla_problem* problem, const void* rows, int32_t src_dtype,
+                  const int32_t* page_table, const int32_t* positions, void* kv_pages,
+                  float* kv_scales, hipStream_t stream);
+
+/*
  * Test hook for the page-table loader: copies, bit for bit, the stored rows
  * of logical token tok[i] of request req[i] (i < n) into out [n, Dc+Dr]
  * (kv_dtype elements), resolving pages with the same device address routine

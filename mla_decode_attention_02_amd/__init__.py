@@ -23,7 +23,7 @@ MLA_ERR_HIP, MLA_ERR_CHECK = -4, -5
 
 EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_decode_split",
            "mla_combine", "mla_balanced_workgroups",
-           "mla_decode_split_balanced", "mla_combine_balanced", "mla_gather_rows",
+           "mla_decode_split_balanced", "mla_combine_balanced", "mla_append_kv", "mla_gather_rows",
            "mla_check_tables", "mla_status_string")
 
 BALANCED_ROWS = 128  # rows per unit of the balanced work list
@@ -66,6 +66,7 @@ def library():
     lib.mla_decode_split_balanced.argtypes = [PP, P, P, P, P, P, P, ctypes.c_float, i32, P, P, P,
                                               P, P, P]
     lib.mla_combine_balanced.argtypes = [PP, i32, P, P, P, P, P, P]
+    lib.mla_append_kv.argtypes = [PP, P, i32, P, P, P, P, P]
     lib.mla_gather_rows.argtypes = [PP, P, P, i32, P, P, P, P]
     lib.mla_check_tables.argtypes = [PP, P, P]
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -280,6 +281,31 @@ def combine(partial_o, partial_lse, *, out_dtype=torch.bfloat16, out=None, lse=N
     _check(library().mla_combine(B, S, R, Dc, _ptr(partial_o), _ptr(partial_lse), code,
                                  _ptr(out), _ptr(lse), _stream()), "mla_combine")
     return out, lse
+
+
+def append_kv(rows, page_table, positions, kv_pages, *, kv_scales=None, d_latent=None):
+    """Paged KV append with packing through ``mla_append_kv``: rows [B, T, D]
+    (float32 or bfloat16) into kv_pages [NP, P, D] (float32, bfloat16 or uint8
+    E4M3 codes with kv_scales [NP, P] float32) at positions[b] + t."""
+    dev = rows.device
+    _require(rows, "rows", dev, ndim=3)
+    _require(page_table, "page_table", dev, dtype=torch.int32, ndim=2)
+    _require(positions, "positions", dev, dtype=torch.int32, ndim=1)
+    _require(kv_pages, "kv_pages", dev, ndim=3)
+    B, T, D = rows.shape
+    NP, P, Dk = kv_pages.shape
+    if Dk != D or page_table.shape[0] != B or positions.numel() != B:
+        raise ValueError("inconsistent shapes")
+    if (kv_scales is None) != (_dtype_code(kv_pages) != MLA_DTYPE_FP8_E4M3):
+        raise ValueError("kv_scales goes with E4M3 pages only")
+    if kv_scales is not None:
+        _require(kv_scales, "kv_scales", dev, dtype=torch.float32)
+    dl = D if d_latent is None else int(d_latent)
+    pr = Problem(B, T, 1, dl, D - dl, P, NP, page_table.shape[1], 0, MLA_DTYPE_BF16,
+                 _dtype_code(kv_pages), MLA_DTYPE_BF16, 0, 0)
+    _check(library().mla_append_kv(ctypes.byref(pr), _ptr(rows), _dtype_code(rows), _ptr(page_table),
+                                   _ptr(positions), _ptr(kv_pages), _ptr(kv_scales), _stream()),
+           "mla_append_kv")
 
 
 def gather_rows(kv_pages, page_table, req, tok, *, d_latent, d_rope=None):

@@ -369,6 +369,24 @@ int mla_combine(int32_t batch, int32_t num_splits, int32_t rows, int32_t d_laten
              : MLA_ERR_HIP;
 }
 
+int mla_append_kv(const mla_problem* problem, const void* rows, int32_t src_dtype,
+                  const int32_t* page_table, const int32_t* positions, void* kv_pages, float* kv_scales,
+                  hipStream_t stream) {
+  const int rc = validate_problem(problem);
+  if (rc) return rc;
+  if (src_dtype != MLA_DTYPE_F32 && src_dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (problem->batch == 0) return MLA_OK;
+  if (!rows || !page_table || !positions || !kv_pages) return MLA_ERR_INVALID_ARG;
+  if ((problem->kv_dtype == MLA_DTYPE_FP8_E4M3) != (kv_scales != nullptr)) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)problem->batch * problem->q_len > INT32_MAX) return MLA_ERR_INVALID_ARG;
+  return mla::launch_append(problem->batch, problem->q_len, problem->d_latent + problem->d_rope,
+                            problem->page_size, problem->max_pages_per_seq, src_dtype,
+                            problem->kv_dtype, rows, page_table, positions, kv_pages, kv_scales,
+                            stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
 int mla_gather_rows(const mla_problem* problem, const void* kv_pages, const int32_t* page_table,
                     int32_t n, const int32_t* req, const int32_t* tok, void* out,
                     hipStream_t stream) {

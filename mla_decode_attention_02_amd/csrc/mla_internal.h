@@ -63,6 +63,11 @@ hipError_t launch_combine(int32_t B, int32_t S, int32_t rows, int32_t Dc, const 
                           const float* part_lse, int32_t out_dtype, void* out, float* lse,
                           hipStream_t stream);
 
+// Paged KV append with packing (see mla_append_kv); arguments validated.
+hipError_t launch_append(int32_t B, int32_t T, int32_t D, int32_t P, int32_t MP, int32_t src_dtype,
+                         int32_t kv_dtype, const void* src, const int32_t* page_table,
+                         const int32_t* positions, void* kv, float* kv_scales, hipStream_t stream);
+
 hipError_t launch_gather(int32_t Dc, int32_t Dr, int32_t P, int32_t MP, int32_t kv_dtype,
                          const void* kv, const int32_t* page_table, int32_t n,
                          const int32_t* req, const int32_t* tok, void* out, hipStream_t stream);

@@ -1204,6 +1204,129 @@ mla_combine_balanced_kernel(int B, int M, int Dc, int NB, const int32_t* __restr
             po, pl, out_dtype, out, idx, lse);
 }
 
+// ------------------------------------------------------------- KV append
+// Paged KV append with packing: token t of request b is stored at logical
+// position pos[b] + t, i.e. page page_table[b][pos / P], slot pos mod P
+// (PagedAttention article on the "推理优化" tag page), as fp32, as bf16
+// (nearest, ties to even) or as OCP E4M3 codes with one fp32 scale per row:
+// s = absmax / 448 (448 = largest finite E4M3, FP8 format table of the
+// quantisation article on the same page; s = 1 for an all-zero row) and each
+// value v stored as the E4M3 code nearest to v / s, ties to even, magnitudes
+// past 448 saturating, the sign kept.
+
+// E4M3 code of an fp32 value: below 2^-6 the format's values are the
+// multiples of 2^-9 (codes 0..8 per sign, 8 being 2^-6 itself); from 2^e
+// (e = -6..8) on the step is 2^(e-3) and the code is (e + 7) << 3 | mantissa.
+__device__ __forceinline__ uint32_t e4m3_encode(float q) {
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t mag = u & 0x7FFFFFFFu;
+  if (mag > 0x7F800000u) return 0x7Fu;  // NaN
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __uint_as_float(mag);
+  if (a >= 448.0f) return sign | 0x7Eu;
+  const int e = (int)(mag >> 23) - 127;  // exponent of a normal fp32 (fp32 subnormals: < -6)
+  if (e < -6) return sign | (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 9));  // exact scaling
+  const float m = __builtin_rintf(__builtin_ldexpf(a, 3 - e));               // 8 .. 16
+  uint32_t code = m == 16.0f ? (uint32_t)(e + 8) << 3 : ((uint32_t)(e + 7) << 3) | ((uint32_t)m - 8u);
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// Four E4M3 codes (byte k = code of q[k]) with the hardware's
+// round-to-nearest-even conversion on the range where it is exact for every
+// fp32 input, and the format's rule outside it: magnitudes at or below 2^-10
+// (half the smallest subnormal step; fp32 subnormals included) become +-0,
+// magnitudes at or past 448 saturate, NaN gives 0x7F.
+__device__ __forceinline__ uint32_t e4m3_encode4(const float (&q)[4]) {
+  float c[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = fabsf(q[k]);
+    c[k] = a <= 0x1p-10f ? __builtin_copysignf(0.0f, q[k]) : (a >= 448.0f ? __builtin_copysignf(448.0f, q[k]) : q[k]);
+  }
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], (int)w, true);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (q[k] != q[k]) w = (w & ~(0xFFu << (8 * k))) | (0x7Fu << (8 * k));
+  return w;
+}
+
+// bf16 bits of an fp32 value: nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint32_t bf16_encode(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// One wavefront per appended row; 4 rows per workgroup.
+__global__ void __launch_bounds__(256)
+mla_append_kernel(int B, int T, int D, int P, int MP, int src_dtype, int kv_dtype,
+                  const void* __restrict__ src, const int32_t* __restrict__ page_table,
+                  const int32_t* __restrict__ pos0, void* __restrict__ kv, float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (idx >= (int64_t)B * T) return;
+  const int b = (int)(idx / T), t = (int)(idx - (int64_t)b * T);
+  const int pos = pos0[b] + t;
+  const int64_t row = (int64_t)page_table[(int64_t)b * MP + pos / P] * P + pos % P;
+  auto value = [&](int d) -> float {
+    return src_dtype == kF32 ? ((const float*)src)[idx * D + d]
+                             : bf16_bits_to_float(((const uint16_t*)src)[idx * D + d]);
+  };
+  if (kv_dtype == kF32) {
+    for (int d = lane; d < D; d += 64) ((float*)kv)[row * D + d] = value(d);
+    return;
+  }
+  if (kv_dtype == kBF16) {
+    for (int d = lane; d < D; d += 64) ((uint16_t*)kv)[row * D + d] = (uint16_t)bf16_encode(value(d));
+    return;
+  }
+  if ((D & 3) == 0 && D <= 1024) {
+    // the row in registers: up to four 4-value chunks per lane, one read
+    float v[4][4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int d = 4 * (lane + 64 * c);
+      if (d < D) {
+        if (src_dtype == kF32) {
+          const floatx4 f = *(const floatx4*)((const float*)src + idx * D + d);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[c][k] = f[k];
+        } else {
+          const uintx2 w = *(const uintx2*)((const uint16_t*)src + idx * D + d);
+          v[c][0] = __uint_as_float(w[0] << 16);
+          v[c][1] = __uint_as_float(w[0] & 0xFFFF0000u);
+          v[c][2] = __uint_as_float(w[1] << 16);
+          v[c][3] = __uint_as_float(w[1] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fabsf(v[c][k]));
+      }
+    }
+    amax = wave_max(amax);
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int d = 4 * (lane + 64 * c);
+      if (d < D) {
+        float q[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q[k] = v[c][k] / s;
+        *(uint32_t*)((uint8_t*)kv + row * D + d) = e4m3_encode4(q);
+      }
+    }
+    if (lane == 0) scales[row] = s;
+    return;
+  }
+  float amax = 0.0f;
+  for (int d = lane; d < D; d += 64) amax = fmaxf(amax, fabsf(value(d)));
+  amax = wave_max(amax);
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  for (int d = lane; d < D; d += 64) ((uint8_t*)kv + row * D)[d] = (uint8_t)e4m3_encode(value(d) / s);
+  if (lane == 0) scales[row] = s;
+}
+
 // ------------------------------------------------------------ gather hook
 __global__ void mla_gather_kernel(int D, int elt, int P, int MP, const char* __restrict__ kv,
                                   const int32_t* __restrict__ page_table, int n,
@@ -1287,6 +1410,16 @@ hipError_t launch_combine_balanced(int32_t B, int32_t M, int32_t Dc, int32_t NB,
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(mla_combine_balanced_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream,
                      B, M, Dc, NB, tile_prefix, (const __bf16*)part_o, part_lse, out_dtype, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(int32_t B, int32_t T, int32_t D, int32_t P, int32_t MP, int32_t src_dtype,
+                         int32_t kv_dtype, const void* src, const int32_t* page_table,
+                         const int32_t* positions, void* kv, float* kv_scales, hipStream_t stream) {
+  const int64_t n = (int64_t)B * T;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_append_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream, B, T, D, P,
+                     MP, src_dtype, kv_dtype, src, page_table, positions, kv, kv_scales);
   return hipGetLastError();
 }
 
