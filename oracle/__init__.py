@@ -59,6 +59,8 @@ def load(rebuild=False):
     lib.orc_e4m3_value.restype = ctypes.c_double
     lib.orc_append_rows.argtypes = [i32, i32, i32, P, P, i32, i32, i32, P, i32, P, P]
     lib.orc_append_rows.restype = ctypes.c_int
+    lib.orc_verify_greedy.argtypes = [i32, i32, i32, P, P, P, P, P]
+    lib.orc_verify_greedy.restype = ctypes.c_int
     lib.orc_e4m3_code.argtypes = [ctypes.c_float]
     lib.orc_e4m3_code.restype = ctypes.c_uint8
     lib.orc_bf16_bits.argtypes = [ctypes.c_float]
@@ -213,3 +215,18 @@ def e4m3_code(q):
 
 def bf16_bits(v):
     return int(load().orc_bf16_bits(float(v)))
+
+
+def verify_greedy(logits, draft):
+    """Greedy linear-chain verification (see orc_verify_greedy).  logits
+    [B, T, V] (any real dtype; compared as exact fp64 values), draft [B, T-1]
+    int32.  Returns (argmax [B, T], accept_len [B], out_tokens [B, T])."""
+    lg = np.ascontiguousarray(logits, dtype=np.float64)
+    B, T, V = lg.shape
+    d = np.ascontiguousarray(draft, dtype=np.int32).reshape(B, max(T - 1, 0))
+    am = np.zeros((B, T), dtype=np.int32)
+    n = np.zeros(B, dtype=np.int32)
+    out = np.zeros((B, T), dtype=np.int32)
+    _check(load().orc_verify_greedy(B, T, V, _ptr(lg), _ptr(d) if d.size else None, _ptr(am), _ptr(n),
+                                    _ptr(out)), "orc_verify_greedy")
+    return am, n, out

@@ -431,6 +431,47 @@ int orc_append_rows(int32_t n_req, int32_t T, int32_t D, const float* src, const
   return ORC_OK;
 }
 
+/*
+ * Greedy verification of a linear chain of drafts (TokenSpeed code-audit
+ * article, complete technology list: speculative decoding entries, greedy
+ * linear-chain verification).  Request b has T query positions: position 0
+ * holds the last accepted token, positions 1..T-1 the drafts d[b][0..T-2].
+ * The target's prediction at position t is p_t = argmax_v logits[b][t][v]
+ * (values compared exactly as stored; the smallest v among equal maxima;
+ * NaN never wins).  Draft i is accepted iff d[b][i] == p_i and every draft
+ * before it was accepted (a running product of matches), so n = number of
+ * leading matches, 0 <= n <= T-1.  The step emits the n accepted drafts and
+ * then the target's own token at the first unaccepted position, p_n (the
+ * bonus token when all drafts pass); out[b] = d[0..n-1], p_n, then -1.
+ * logits: [B, T, V] as fp64 values of the stored numbers.
+ */
+int orc_verify_greedy(int32_t B, int32_t T, int32_t V, const double* logits, const int32_t* draft,
+                      int32_t* argmax, int32_t* accept_len, int32_t* out) {
+  if (B < 0 || T < 1 || V < 1 || !logits || (T > 1 && !draft) || !argmax || !accept_len || !out)
+    return ORC_BAD_ARG;
+  for (int b = 0; b < B; ++b) {
+    for (int t = 0; t < T; ++t) {
+      const double* row = logits + ((size_t)b * T + t) * V;
+      int best = -1;
+      for (int v = 0; v < V; ++v) {
+        if (isnan(row[v])) continue;
+        if (best < 0 || row[v] > row[best]) best = v;
+      }
+      argmax[(size_t)b * T + t] = best < 0 ? 0 : best;
+    }
+    int n = 0;
+    while (n < T - 1 && draft[(size_t)b * (T - 1) + n] == argmax[(size_t)b * T + n]) ++n;
+    accept_len[b] = n;
+    for (int i = 0; i < T; ++i) {
+      int32_t tok = -1;
+      if (i < n) tok = draft[(size_t)b * (T - 1) + i];
+      else if (i == n) tok = argmax[(size_t)b * T + n];
+      out[(size_t)b * T + i] = tok;
+    }
+  }
+  return ORC_OK;
+}
+
 /* E4M3 code of one fp32 value (for pinning the encoder on its own). */
 uint8_t orc_e4m3_code(float q) { return e4m3_code_of(q); }
 uint16_t orc_bf16_bits(float v) { return bf16_bits_of(v); }

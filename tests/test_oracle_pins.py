@@ -577,3 +577,48 @@ def test_append_fp8_matches_generator_encoder():
     order = [(2, s) for s in range(16)] + [(0, s) for s in range(16)] + [(1, s) for s in range(8)]
     for t, (pg, sl) in enumerate(order):
         assert np.array_equal(kv[pg, sl], codes[t]) and sc[pg, sl] == scales[t]
+
+
+# -------------------------------------------------- greedy chain verification
+
+def test_verify_argmax_matches_numpy_first_occurrence():
+    """p_t against numpy's argmax (first index among equal maxima), with ties
+    made frequent by rounding the logits to bf16 and by planting copies."""
+    rng = np.random.default_rng(21)
+    lg = torch.from_numpy(rng.standard_normal((6, 4, 3000)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    lg[0, 0, 100] = lg[0, 0, 2000] = lg[0, 0].max() + 1.0   # an exact tie, smaller index wins
+    lg[1, 2, :] = 0.5                                        # all equal: index 0
+    am, _, _ = oracle.verify_greedy(lg, np.zeros((6, 3), dtype=np.int32))
+    assert np.array_equal(am, lg.argmax(axis=2))
+    assert am[0, 0] == 100 and am[1, 2] == 0
+
+
+def test_verify_nan_never_wins():
+    lg = np.array([[[np.nan, 1.0, 3.0, np.nan, 2.0]]])
+    am, n, out = oracle.verify_greedy(lg, np.zeros((1, 0), dtype=np.int32))
+    assert am[0, 0] == 2 and n[0] == 0 and out[0, 0] == 2
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 7])
+def test_verify_acceptance_is_the_run_of_leading_matches(T):
+    """Drafts built from the target's own predictions with one planted
+    mismatch at k: exactly k drafts pass (later matches do not count), the
+    output is those drafts, then p_k, then -1."""
+    rng = np.random.default_rng(22 + T)
+    B, V = 3 * T, 50
+    lg = rng.standard_normal((B, T, V))
+    p = lg.argmax(axis=2)
+    draft = p[:, : T - 1].astype(np.int32).copy()
+    planted = []
+    for b in range(B):
+        k = b % T  # k = T - 1: no mismatch, every draft passes and p_{T-1} is the bonus
+        if k < T - 1:
+            draft[b, k] = (p[b, k] + 1) % V
+        planted.append(k)
+    am, n, out = oracle.verify_greedy(lg, draft)
+    assert np.array_equal(am, p)
+    for b in range(B):
+        k = planted[b]
+        assert n[b] == k
+        assert list(out[b, :k]) == list(draft[b, :k]) and out[b, k] == p[b, k]
+        assert (out[b, k + 1:] == -1).all()
