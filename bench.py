@@ -250,6 +250,64 @@ def bench_append(mla, args):
     print(json.dumps(line), flush=True)
 
 
+def bench_verify(mla, args):
+    """Greedy chain verification after the speculative-decode step: 256
+    requests x 4 positions of bf16 logits over a 129280-token vocabulary
+    (DeepSeek-V3's size, assumed: the pages state none).  HBM-bound: the
+    algorithmic bytes are the logits plus drafts read and the results written."""
+    B, T, V = 256, 4, 129280
+    rng = np.random.default_rng(2025)
+    lg = torch.from_numpy(rng.standard_normal((B, T, V)).astype(np.float32)).to(torch.bfloat16).cuda()
+    draft = torch.from_numpy(rng.integers(0, V, size=(B, T - 1)).astype(np.int32)).cuda()
+    am = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    n = torch.empty((B,), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    import ctypes
+    lib = mla.library()
+    P_ = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    call = (B, T, V, P_(lg), mla.MLA_DTYPE_BF16, P_(draft), P_(am), P_(n), P_(out), stream)
+    for _ in range(args.warmup):
+        if lib.mla_verify_greedy(*call):
+            raise RuntimeError("mla_verify_greedy failed")
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        lib.mla_verify_greedy(*call)
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = B * T * V * 2 + B * (T - 1) * 4 + B * (2 * T + 1) * 4
+    achieved = nbytes / (k_ms / 1e3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        sub = 8
+        vals = lg[:sub].float().cpu().numpy()
+        t1 = time.perf_counter()
+        oracle.verify_greedy(vals, draft[:sub].cpu().numpy())
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(sub * T * V * 2 / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{sub} of {B} requests x {T} positions, single-threaded C oracle, {dt:.2f} s"}
+    line = {
+        "metric": "greedy draft verification, logits GB/s (1 MI355X)", "value": round(achieved, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 logits, int32 tokens",
+        "data": "synthetic (seeded N(0,1) logits rounded to bf16, random drafts)",
+        "config": {"workload": "verify_greedy", "requests": B, "positions": T, "vocab": V,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "mla_verify_kernel",
+                     "per_launch_algorithmic": nbytes, "kernel_avg_ms": round(k_ms, 5)},
+        "cpu_baseline": cpu,
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,8 +324,9 @@ def main():
     ap.add_argument("--pmc-summary", metavar="DIR",
                     help="summarise FETCH_SIZE/WRITE_SIZE rocprofv3 CSVs in DIR and exit")
     ap.add_argument("--pmc-out", metavar="FILE", help="where --pmc-summary writes its summary")
-    ap.add_argument("--op", choices=("decode", "append"), default="decode",
-                    help="decode (the default hot path) or the paged KV append with FP8 packing")
+    ap.add_argument("--op", choices=("decode", "append", "verify"), default="decode",
+                    help="decode (the default hot path), the paged KV append with FP8 packing, "
+                         "or the greedy verification of speculative drafts")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, args.workload, args.calib_copy_mib or 1024,
@@ -282,6 +341,9 @@ def main():
     torch.cuda.set_device(0)
     if args.op == "append":
         bench_append(mla, args)
+        return
+    if args.op == "verify":
+        bench_verify(mla, args)
         return
 
     w = next(x for x in synth.WORKLOADS if x.name == args.workload)

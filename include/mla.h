@@ -243,6 +243,26 @@ int mla_append_kv(const mla_problem* problem, const void* rows, int32_t src_dtyp
                   float* kv_scales, hipStream_t stream);
 
 /*
+ * Greedy verification of a linear chain of speculative drafts, the step after
+ * the speculative-decode attention (TokenSpeed code-audit article, complete
+ * technology list, speculative decoding: greedy linear-chain verification).
+ * Request b has T = num_positions (1..64) positions: position 0 holds the
+ * last accepted token, positions 1..T-1 the drafts.
+ *   logits     [B, T, vocab] logits_dtype (F32 or BF16), device
+ *   draft      [B, T-1] int32 draft tokens (may be NULL when T == 1)
+ *   argmax     [B, T] int32 out: p_t = argmax_v logits[b][t][v], stored values
+ *              compared exactly, the smallest v among equal maxima, NaN never
+ *              chosen (0 if every entry is NaN)
+ *   accept_len [B] int32 out: n = number of leading drafts with
+ *              draft[b][i] == p_i (a draft after a mismatch never passes)
+ *   out_tokens [B, T] int32 out: draft[b][0..n-1], then p_n (the target's own
+ *              token, the bonus token when every draft passes), then -1
+ */
+int mla_verify_greedy(int32_t batch, int32_t num_positions, int32_t vocab, const void* logits,
+                      int32_t logits_dtype, const int32_t* draft, int32_t* argmax, int32_t* accept_len,
+                      int32_t* out_tokens, hipStream_t stream);
+
+/*
  * Test hook for the page-table loader: copies, bit for bit, the stored rows
  * of logical token tok[i] of request req[i] (i < n) into out [n, Dc+Dr]
  * (kv_dtype elements), resolving pages with the same device address routine

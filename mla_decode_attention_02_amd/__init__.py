@@ -23,7 +23,8 @@ MLA_ERR_HIP, MLA_ERR_CHECK = -4, -5
 
 EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_decode_split",
            "mla_combine", "mla_balanced_workgroups",
-           "mla_decode_split_balanced", "mla_combine_balanced", "mla_append_kv", "mla_gather_rows",
+           "mla_decode_split_balanced", "mla_combine_balanced", "mla_append_kv", "mla_verify_greedy",
+           "mla_gather_rows",
            "mla_check_tables", "mla_status_string")
 
 BALANCED_ROWS = 128  # rows per unit of the balanced work list
@@ -67,6 +68,7 @@ def library():
                                               P, P, P]
     lib.mla_combine_balanced.argtypes = [PP, i32, P, P, P, P, P, P]
     lib.mla_append_kv.argtypes = [PP, P, i32, P, P, P, P, P]
+    lib.mla_verify_greedy.argtypes = [i32, i32, i32, P, i32, P, P, P, P, P]
     lib.mla_gather_rows.argtypes = [PP, P, P, i32, P, P, P, P]
     lib.mla_check_tables.argtypes = [PP, P, P]
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -306,6 +308,26 @@ def append_kv(rows, page_table, positions, kv_pages, *, kv_scales=None, d_latent
     _check(library().mla_append_kv(ctypes.byref(pr), _ptr(rows), _dtype_code(rows), _ptr(page_table),
                                    _ptr(positions), _ptr(kv_pages), _ptr(kv_scales), _stream()),
            "mla_append_kv")
+
+
+def verify_greedy(logits, draft=None):
+    """Greedy linear-chain verification through ``mla_verify_greedy``: logits
+    [B, T, V] (float32 or bfloat16), draft [B, T-1] int32.  Returns
+    (argmax [B, T], accept_len [B], out_tokens [B, T]) int32 tensors."""
+    dev = logits.device
+    _require(logits, "logits", dev, ndim=3)
+    B, T, V = logits.shape
+    if T > 1:
+        _require(draft, "draft", dev, dtype=torch.int32, ndim=2)
+        if tuple(draft.shape) != (B, T - 1):
+            raise ValueError("draft must be [B, T-1]")
+    am = torch.empty((B, T), dtype=torch.int32, device=dev)
+    n = torch.empty((B,), dtype=torch.int32, device=dev)
+    out = torch.empty((B, T), dtype=torch.int32, device=dev)
+    _check(library().mla_verify_greedy(B, T, V, _ptr(logits), _dtype_code(logits),
+                                       _ptr(draft) if T > 1 else None, _ptr(am), _ptr(n), _ptr(out),
+                                       _stream()), "mla_verify_greedy")
+    return am, n, out
 
 
 def gather_rows(kv_pages, page_table, req, tok, *, d_latent, d_rope=None):

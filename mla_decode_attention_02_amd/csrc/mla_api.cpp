@@ -387,6 +387,22 @@ int mla_append_kv(const mla_problem* problem, const void* rows, int32_t src_dtyp
              : MLA_ERR_HIP;
 }
 
+int mla_verify_greedy(int32_t batch, int32_t num_positions, int32_t vocab, const void* logits,
+                      int32_t logits_dtype, const int32_t* draft, int32_t* argmax, int32_t* accept_len,
+                      int32_t* out_tokens, hipStream_t stream) {
+  if (batch < 0 || num_positions < 1 || vocab < 1) return MLA_ERR_INVALID_ARG;
+  if (logits_dtype != MLA_DTYPE_F32 && logits_dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (num_positions > 64) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * num_positions * vocab > (int64_t)1 << 40) return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!logits || !argmax || !accept_len || !out_tokens || (num_positions > 1 && !draft))
+    return MLA_ERR_INVALID_ARG;
+  return mla::launch_verify(batch, num_positions, vocab, logits_dtype, logits, draft, argmax, accept_len,
+                            out_tokens, stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
 int mla_gather_rows(const mla_problem* problem, const void* kv_pages, const int32_t* page_table,
                     int32_t n, const int32_t* req, const int32_t* tok, void* out,
                     hipStream_t stream) {

@@ -68,6 +68,11 @@ hipError_t launch_append(int32_t B, int32_t T, int32_t D, int32_t P, int32_t MP,
                          int32_t kv_dtype, const void* src, const int32_t* page_table,
                          const int32_t* positions, void* kv, float* kv_scales, hipStream_t stream);
 
+// Greedy chain verification (see mla_verify_greedy); T <= 64, arguments validated.
+hipError_t launch_verify(int32_t B, int32_t T, int32_t V, int32_t dtype, const void* logits,
+                         const int32_t* draft, int32_t* argmax, int32_t* accept_len, int32_t* out,
+                         hipStream_t stream);
+
 hipError_t launch_gather(int32_t Dc, int32_t Dr, int32_t P, int32_t MP, int32_t kv_dtype,
                          const void* kv, const int32_t* page_table, int32_t n,
                          const int32_t* req, const int32_t* tok, void* out, hipStream_t stream);

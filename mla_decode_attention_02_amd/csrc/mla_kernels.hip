@@ -1327,6 +1327,102 @@ mla_append_kernel(int B, int T, int D, int P, int MP, int src_dtype, int kv_dtyp
   if (lane == 0) scales[row] = s;
 }
 
+// ------------------------------------------------- greedy chain verification
+// Greedy verification of a linear chain of drafts (TokenSpeed code-audit
+// article, technology list, speculative decoding: greedy linear-chain
+// verification).  Request b has T positions; position 0 holds the last
+// accepted token and positions 1..T-1 the drafts d[0..T-2].  The target's
+// token at position t is p_t = argmax_v logits[b][t][v] (stored values
+// compared exactly, the smallest index among equal maxima, NaN never wins, 0
+// when every entry is NaN).  Draft i passes iff d[i] == p_i and every draft
+// before it passed; with n passing, out = d[0..n-1], p_n, then -1.
+// One workgroup per request; the rows are scanned one after another by all
+// threads, each keeping the first maximum of its own (increasing) indices.
+struct ArgMax {
+  float v;
+  int i;  // kNone: nothing seen yet
+};
+constexpr int kNone = 0x7FFFFFFF;
+__device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
+  if (a.i == kNone) return b;
+  if (b.i == kNone) return a;
+  if (b.v > a.v) return b;
+  if (a.v > b.v) return a;
+  return b.i < a.i ? b : a;
+}
+__device__ __forceinline__ void take(ArgMax& a, float v, int i) {
+  if (v == v && (a.i == kNone || v > a.v)) a = ArgMax{v, i};  // indices arrive in increasing order
+}
+
+__global__ void __launch_bounds__(1024)
+mla_verify_kernel(int T, int V, int dtype, const void* __restrict__ logits, const int32_t* __restrict__ draft,
+                  int32_t* __restrict__ argmax, int32_t* __restrict__ accept_len, int32_t* __restrict__ out) {
+  __shared__ float red_v[16];
+  __shared__ int red_i[16];
+  __shared__ int best_sh[64];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int t = 0; t < T; ++t) {  // T <= 64 (checked on the host)
+    const int64_t base = ((int64_t)b * T + t) * V;
+    ArgMax a{0.0f, kNone};
+    if (dtype == kBF16 && (V & 7) == 0) {
+      const uintx4* row = (const uintx4*)((const uint16_t*)logits + base);
+      const int nc = V >> 3;
+      auto take8 = [&](const uintx4& w, int c) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          take(a, __uint_as_float(w[k] << 16), 8 * c + 2 * k);
+          take(a, __uint_as_float(w[k] & 0xFFFF0000u), 8 * c + 2 * k + 1);
+        }
+      };
+      int c = tid;
+      for (; c + 3 * 1024 < nc; c += 4 * 1024) {  // four 16-byte loads in flight per thread
+        uintx4 w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = row[c + u * 1024];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) take8(w[u], c + u * 1024);
+      }
+      for (; c < nc; c += 1024) take8(row[c], c);
+    } else if (dtype == kF32 && (V & 3) == 0) {
+      const floatx4* row = (const floatx4*)((const float*)logits + base);
+      const int nc = V >> 2;
+      for (int c = tid; c < nc; c += 1024) {
+        const floatx4 w = row[c];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) take(a, w[k], 4 * c + k);
+      }
+    } else {
+      for (int v = tid; v < V; v += 1024)
+        take(a, dtype == kF32 ? ((const float*)logits)[base + v]
+                              : bf16_bits_to_float(((const uint16_t*)logits)[base + v]), v);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const ArgMax o{__shfl_xor(a.v, off, 64), __shfl_xor(a.i, off, 64)};
+      a = better(a, o);
+    }
+    if (lane == 0) {
+      red_v[wave] = a.v;
+      red_i[wave] = a.i;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      ArgMax m{red_v[0], red_i[0]};
+      for (int w = 1; w < 16; ++w) m = better(m, ArgMax{red_v[w], red_i[w]});
+      best_sh[t] = m.i == kNone ? 0 : m.i;
+      argmax[(int64_t)b * T + t] = best_sh[t];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {  // the run of leading matches
+    int n = 0;
+    while (n < T - 1 && draft[(int64_t)b * (T - 1) + n] == best_sh[n]) ++n;
+    accept_len[b] = n;
+    for (int i = 0; i < T; ++i)
+      out[(int64_t)b * T + i] = i < n ? draft[(int64_t)b * (T - 1) + i] : (i == n ? best_sh[n] : -1);
+  }
+}
+
 // ------------------------------------------------------------ gather hook
 __global__ void mla_gather_kernel(int D, int elt, int P, int MP, const char* __restrict__ kv,
                                   const int32_t* __restrict__ page_table, int n,
@@ -1420,6 +1516,15 @@ hipError_t launch_append(int32_t B, int32_t T, int32_t D, int32_t P, int32_t MP,
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(mla_append_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream, B, T, D, P,
                      MP, src_dtype, kv_dtype, src, page_table, positions, kv, kv_scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(int32_t B, int32_t T, int32_t V, int32_t dtype, const void* logits,
+                         const int32_t* draft, int32_t* argmax, int32_t* accept_len, int32_t* out,
+                         hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_verify_kernel, dim3((unsigned)B), dim3(1024), 0, stream, T, V, dtype, logits, draft,
+                     argmax, accept_len, out);
   return hipGetLastError();
 }
 
