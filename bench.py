@@ -324,6 +324,8 @@ def main():
     ap.add_argument("--pmc-summary", metavar="DIR",
                     help="summarise FETCH_SIZE/WRITE_SIZE rocprofv3 CSVs in DIR and exit")
     ap.add_argument("--pmc-out", metavar="FILE", help="where --pmc-summary writes its summary")
+    ap.add_argument("--cascade", action="store_true",
+                    help="decode with mla_decode_cascade over the workload's shared prefix")
     ap.add_argument("--op", choices=("decode", "append", "verify"), default="decode",
                     help="decode (the default hot path), the paged KV append with FP8 packing, "
                          "or the greedy verification of speculative drafts")
@@ -404,10 +406,26 @@ def main():
                         P(slot_l), stream) for d in sets]
         bcomb_args = (ctypes.byref(prs), nw, P(prefix), P(slot_o), P(slot_l), P(out), P(lse), stream)
 
+    if args.cascade:
+        if not w.shared_prefix:
+            raise SystemExit("--cascade needs a workload with a shared prefix")
+        need = ctypes.c_size_t(0)
+        lib.mla_cascade_workspace_size(ctypes.byref(prs), w.shared_prefix, ctypes.byref(need))
+        cws = torch.empty(max(1, need.value), dtype=torch.uint8, device="cuda")
+        casc_args = [(ctypes.byref(prs), P(d["q_abs"]), P(d["q_rope"]), P(d["kv"]), P(d["kv_scales"]),
+                      P(d["page_table"]), P(d["seq_lens"]), ctypes.c_float(scale), w.shared_prefix, P(out),
+                      P(lse), P(cws), cws.numel(), stream) for d in sets]
+        balanced = False
+
     def step(i, evs=None):
         if evs is not None:
             evs[0].record()
-        if balanced:
+        if args.cascade:
+            # split and merge in one call: the "split" events bracket both
+            rc = lib.mla_decode_cascade(*casc_args[i % copies])
+            if evs is not None:
+                evs[1].record()
+        elif balanced:
             rc = lib.mla_decode_split_balanced(*bsplit_args[i % copies])
             if evs is not None:
                 evs[1].record()
@@ -484,7 +502,8 @@ def main():
         "config": {"workload": w.name, "batch": B, "q_len": T, "heads": H, "d_latent": w.d_latent,
                    "d_rope": w.d_rope, "page_size": w.page_size, "seq_lens": seq_desc,
                    "shared_prefix": w.shared_prefix, "causal": w.causal,
-                   "plan": (f"balanced work list, {nw} workgroups" if balanced
+                   "plan": ("cascade over the shared prefix (split and merge timed together)" if args.cascade
+                            else f"balanced work list, {nw} workgroups" if balanced
                             else f"uniform, {S} chunks per request"),
                    "kv_copies_rotated": copies, "parallelism": "single GPU"},
         "tokens_per_s": round(tokens_per_s, 1),

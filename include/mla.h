@@ -219,6 +219,28 @@ int mla_combine_balanced(const mla_problem* problem, int32_t num_workgroups,
                          void* out, float* lse, hipStream_t stream);
 
 /*
+ * Cascade decode over a shared prefix (the zero-copy article: requests share
+ * prefix KV by reference; the pages stress prefix reuse): the first
+ * prefix_len tokens (a multiple of page_size) are split into chunks with the
+ * same bounds for every request, each request's remaining tokens
+ * [prefix_len, L_b) into chunks of its own, and the chunk partials are merged
+ * by log-sum-exp as in mla_combine().  The workgroups that read one prefix
+ * chunk for the different requests are dealt onto one XCD and run together,
+ * so when the requests' tables alias the prefix pages each prefix tile is
+ * read from HBM once and served from that XCD's L2 to the others.  Results
+ * never depend on the aliasing (every workgroup reads through its own
+ * request's table): they equal mla_decode()'s up to rounding for any
+ * prefix_len, including requests shorter than the prefix.  MFMA-kernel
+ * shapes only (else MLA_ERR_UNSUPPORTED); workspace from
+ * mla_cascade_workspace_size(); other arguments as for mla_decode().
+ */
+int mla_cascade_workspace_size(const mla_problem* problem, int32_t prefix_len, size_t* bytes);
+int mla_decode_cascade(const mla_problem* problem, const void* q_absorbed, const void* q_rope,
+                       const void* kv_pages, const float* kv_scales, const int32_t* page_table,
+                       const int32_t* seq_lens, float scale, int32_t prefix_len, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Paged KV append with packing: the write that fills the cache the decode
  * reads.  problem->batch = B requests, problem->q_len = T new tokens each,
  * rows of D = d_latent + d_rope values; page_size, num_pages,

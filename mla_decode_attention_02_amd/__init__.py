@@ -23,7 +23,8 @@ MLA_ERR_HIP, MLA_ERR_CHECK = -4, -5
 
 EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_decode_split",
            "mla_combine", "mla_balanced_workgroups",
-           "mla_decode_split_balanced", "mla_combine_balanced", "mla_append_kv", "mla_verify_greedy",
+           "mla_decode_split_balanced", "mla_combine_balanced", "mla_cascade_workspace_size",
+           "mla_decode_cascade", "mla_append_kv", "mla_verify_greedy",
            "mla_gather_rows",
            "mla_check_tables", "mla_status_string")
 
@@ -67,6 +68,8 @@ def library():
     lib.mla_decode_split_balanced.argtypes = [PP, P, P, P, P, P, P, ctypes.c_float, i32, P, P, P,
                                               P, P, P]
     lib.mla_combine_balanced.argtypes = [PP, i32, P, P, P, P, P, P]
+    lib.mla_cascade_workspace_size.argtypes = [PP, i32, ctypes.POINTER(sz)]
+    lib.mla_decode_cascade.argtypes = [PP, P, P, P, P, P, P, ctypes.c_float, i32, P, P, P, sz, P]
     lib.mla_append_kv.argtypes = [PP, P, i32, P, P, P, P, P]
     lib.mla_verify_greedy.argtypes = [i32, i32, i32, P, i32, P, P, P, P, P]
     lib.mla_gather_rows.argtypes = [PP, P, P, i32, P, P, P, P]
@@ -192,6 +195,32 @@ def decode(q_abs, q_rope, kv_pages, page_table, seq_lens, scale, *, kv_scales=No
                                 _ptr(kv_scales), _ptr(page_table), _ptr(seq_lens),
                                 ctypes.c_float(float(scale)), _ptr(out), _ptr(lse),
                                 _ptr(workspace), ws_bytes, _stream()), "mla_decode")
+    return out, lse
+
+
+def decode_cascade(q_abs, q_rope, kv_pages, page_table, seq_lens, scale, prefix_len, *, kv_scales=None,
+                   causal=False, max_seq_len=0, out=None, lse=None, workspace=None, out_dtype=None):
+    """Cascade decode over a shared prefix of prefix_len tokens (mla_decode_cascade).
+    Returns (out, lse)."""
+    _validate(q_abs, q_rope, kv_pages, page_table, seq_lens, kv_scales)
+    pr = make_problem(q_abs, q_rope, kv_pages, page_table, causal=causal, max_seq_len=max_seq_len,
+                      out_dtype=out_dtype)
+    dev = q_abs.device
+    B, T, H, Dc = q_abs.shape
+    if out is None:
+        out = torch.empty((B, T, H, Dc), dtype=_torch_dtype(pr.out_dtype), device=dev)
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    need = ctypes.c_size_t(0)
+    _check(library().mla_cascade_workspace_size(ctypes.byref(pr), int(prefix_len), ctypes.byref(need)),
+           "mla_cascade_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(max(1, need.value), dtype=torch.uint8, device=dev)
+    _check(library().mla_decode_cascade(ctypes.byref(pr), _ptr(q_abs), _ptr(q_rope), _ptr(kv_pages),
+                                        _ptr(kv_scales), _ptr(page_table), _ptr(seq_lens),
+                                        ctypes.c_float(float(scale)), int(prefix_len), _ptr(out), _ptr(lse),
+                                        _ptr(workspace), workspace.numel(), _stream()),
+           "mla_decode_cascade")
     return out, lse
 
 

@@ -189,6 +189,34 @@ int run_checked_mode(const mla_problem* pr, const int32_t* page_table, const int
   return mla_check_tables(pr, pt.data(), sl.data());
 }
 
+// Cascade plan: chunks of about the same length for the shared prefix and
+// for each request's suffix, sized so that the grid reaches about
+// kTargetWorkgroups workgroups.
+void cascade_plan(const mla_problem* pr, int32_t prefix_len, int32_t* Sp, int32_t* Ss) {
+  const int64_t P = pr->page_size;
+  const int64_t max_len = effective_max_len(pr);
+  const int64_t groups = ((int64_t)pr->q_len * pr->num_heads + 127) / 128;
+  const int64_t units = (int64_t)(pr->batch > 0 ? pr->batch : 1) * groups;
+  int64_t chunk = (units * max_len + kTargetWorkgroups - 1) / kTargetWorkgroups;
+  chunk = (chunk + P - 1) / P * P;
+  if (chunk < P) chunk = P;
+  const int64_t suffix = max_len > prefix_len ? max_len - prefix_len : 0;
+  int64_t sp = (prefix_len + chunk - 1) / chunk, ss = (suffix + chunk - 1) / chunk;
+  if (sp < 1) sp = 1;
+  if (ss < 1) ss = 1;
+  *Sp = (int32_t)(sp < kAutoMaxSplits ? sp : kAutoMaxSplits);
+  *Ss = (int32_t)(ss < kAutoMaxSplits ? ss : kAutoMaxSplits);
+}
+
+int cascade_check(const mla_problem* pr, int32_t prefix_len) {
+  const int rc = validate_problem(pr);
+  if (rc) return rc;
+  if (prefix_len < 0 || prefix_len % pr->page_size != 0 ||
+      (int64_t)prefix_len > (int64_t)pr->max_pages_per_seq * pr->page_size)
+    return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -351,6 +379,50 @@ int mla_combine_balanced(const mla_problem* problem, int32_t num_workgroups,
   return mla::launch_combine_balanced(problem->batch, M, problem->d_latent, num_workgroups,
                                       tile_prefix, slot_o, slot_lse, problem->out_dtype, out, lse,
                                       stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+int mla_cascade_workspace_size(const mla_problem* problem, int32_t prefix_len, size_t* bytes) {
+  const int rc = cascade_check(problem, prefix_len);
+  if (rc) return rc;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  int32_t Sp, Ss;
+  cascade_plan(problem, prefix_len, &Sp, &Ss);
+  *bytes = partial_bytes(problem, Sp + Ss);
+  return MLA_OK;
+}
+
+int mla_decode_cascade(const mla_problem* problem, const void* q_absorbed, const void* q_rope,
+                       const void* kv_pages, const float* kv_scales, const int32_t* page_table,
+                       const int32_t* seq_lens, float scale, int32_t prefix_len, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = cascade_check(problem, prefix_len);
+  if (rc) return rc;
+  rc = validate_inputs(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table, seq_lens);
+  if (rc) return rc;
+  if (problem->batch == 0) return MLA_OK;
+  if (!out) return MLA_ERR_INVALID_ARG;
+  int32_t Sp, Ss;
+  cascade_plan(problem, prefix_len, &Sp, &Ss);
+  const int32_t S = Sp + Ss;
+  const size_t need = partial_bytes(problem, S);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0) return MLA_ERR_WORKSPACE;
+  SplitParams p = make_params(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table, seq_lens,
+                              scale, S);
+  if (mla::pick_kernel(p) == mla::Kernel::kGeneric) return MLA_ERR_UNSUPPORTED;
+  rc = run_checked_mode(problem, page_table, seq_lens, stream);
+  if (rc) return rc;
+  const int32_t rows = problem->q_len * problem->num_heads;
+  const size_t o_bytes = (size_t)problem->batch * S * rows * problem->d_latent * sizeof(float);
+  p.Sp = Sp;
+  p.prefix_len = prefix_len;
+  p.write_final = false;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)((char*)workspace + ((o_bytes + 255) & ~(size_t)255));
+  if (mla::launch_split(p, stream) != hipSuccess) return MLA_ERR_HIP;
+  return mla::launch_combine(problem->batch, S, rows, problem->d_latent, p.part_o, p.part_lse,
+                             problem->out_dtype, out, lse, stream) == hipSuccess
              ? MLA_OK
              : MLA_ERR_HIP;
 }

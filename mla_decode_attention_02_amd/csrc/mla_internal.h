@@ -32,7 +32,12 @@ struct SplitParams {
   // the 32-token tiles of all units (request, group of kBalancedRows rows)
   // are cut into NB equal contiguous ranges, one per workgroup.
   int32_t NB;
-  int32_t* tile_prefix;        // [B * groups + 1] exclusive prefix of tiles per unit,
+  int32_t* tile_prefix;
+  // Cascade (uniform chunks only; Sp == 0 disables it): chunks 0..Sp-1 split
+  // the first prefix_len tokens (a prefix every request shares) with the same
+  // page-aligned bounds for all requests, chunks Sp..S-1 split [prefix_len, L_b).
+  int32_t Sp;
+  int32_t prefix_len;        // [B * groups + 1] exclusive prefix of tiles per unit,
                                // written by workgroup 0 for the merge
 };
 

@@ -376,7 +376,19 @@ mla_split_mfma(SplitParams p, int groups) {
   int ub = 0, ug = 0, us = 0;
   int wx = 0, wx1 = 0;
   int wu = 0, wk = 0, wsu = 0;  // balanced: current unit and its first tile
-  if (p.NB == 0) {
+  if (p.NB == 0 && p.Sp > 0) {
+    // Cascade: chunk s runs on XCD s mod 8, where its workgroups for every
+    // request and row group take consecutive slots, so that the workgroups
+    // reading one shared-prefix chunk run together and share that XCD's L2.
+    const int x = blockIdx.x;
+    const int xcd = x & 7, slot = x >> 3;
+    const int per = p.B * groups;
+    const int sl8 = slot / per, rem = slot - sl8 * per;
+    us = 8 * sl8 + xcd;
+    if (us >= p.S) return;
+    ub = rem / groups;
+    ug = rem - ub * groups;
+  } else if (p.NB == 0) {
     const int x = blockIdx.x;
     const int xcd = x & 7, slot = x >> 3;
     const int k8 = slot / groups;
@@ -462,7 +474,18 @@ mla_split_mfma(SplitParams p, int groups) {
     b = ub;
     g = ug;
     L = uniform_load(p.seq_lens + b);
-    chunk_span(L, p.S, p.P, us, &cb, &ce);
+    if (p.Sp == 0) {
+      chunk_span(L, p.S, p.P, us, &cb, &ce);
+    } else if (us < p.Sp) {  // shared-prefix chunk: the same bounds for every request
+      chunk_span(p.prefix_len, p.Sp, p.P, us, &cb, &ce);
+      cb = cb < L ? cb : L;
+      ce = ce < L ? ce : L;
+    } else {  // suffix chunk of [prefix_len, L)
+      const int Ls = L > p.prefix_len ? L - p.prefix_len : 0;
+      chunk_span(Ls, p.S - p.Sp, p.P, us - p.Sp, &cb, &ce);
+      cb += p.prefix_len;
+      ce += p.prefix_len;
+    }
     final_out = p.write_final;
     drow = final_out ? (int64_t)b * M + (int64_t)g * kRows
                      : ((int64_t)b * p.S + us) * M + (int64_t)g * kRows;
@@ -1446,7 +1469,9 @@ hipError_t launch_mfma(const SplitParams& p, hipStream_t stream) {
   const int groups = (M + kRows - 1) / kRows;
   static_assert(kRows == kBalancedRows, "balanced units are one workgroup of rows");
   const int units = p.B * p.S;
-  const int64_t blocks = p.NB > 0 ? p.NB : 8LL * groups * ((units + 7) / 8);
+  const int64_t blocks = p.NB > 0   ? (int64_t)p.NB
+                         : p.Sp > 0 ? 8LL * ((p.S + 7) / 8) * p.B * groups  // cascade: chunk-major per XCD
+                                    : 8LL * groups * ((units + 7) / 8);
   // + restart requests + plan scratch
   const size_t lds = (size_t)STAGES * Tile<FP8>::kStage + 8 * WAVES + 4 * (WAVES + 2);
   static std::once_flag once;

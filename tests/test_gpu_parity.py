@@ -183,6 +183,41 @@ def test_balanced_stages(mla, nw):
         assert np.array_equal(o, o2) and np.array_equal(l, l2)
 
 
+# ------------------------------------------------------------ cascade decode
+
+@pytest.mark.parametrize("case", ["agentic", "short_requests", "fp8", "causal"])
+def test_cascade_decode_matches_oracle(mla, case):
+    """Cascade decode (shared-prefix chunks + per-request suffix chunks, merged)
+    against the unsplit oracle: with the prefix pages aliased as in the agentic
+    workload, with requests shorter than the prefix, on FP8 KV, and with the
+    causal drafts."""
+    if case == "agentic":
+        w = small(2, batch=4, seq_lens=("fixed", (700, 1000, 1500, 3000)), shared_prefix=512,
+                  decoys=4, index=50)
+        prefix = 512
+    elif case == "short_requests":
+        w = small(1, batch=3, seq_lens=("fixed", (100, 700, 2000)), decoys=2, index=51)
+        prefix = 640
+    elif case == "fp8":
+        w = small(4, batch=3, seq_lens=("fixed", (900, 1300, 2600)), decoys=2, index=52)
+        prefix = 256
+    else:
+        w = small(3, batch=3, seq_lens=("fixed", (70, 500, 1200)), decoys=2, index=53)
+        prefix = 128
+    inp = synth.make_inputs(w)
+    dev = to_device(inp)
+    out, lse = mla.decode_cascade(dev["q_abs"], dev["q_rope"], dev["kv"], dev["page_table"],
+                                  dev["seq_lens"], float(inp["scale"]), prefix, kv_scales=dev["kv_scales"],
+                                  causal=w.causal, max_seq_len=w.max_seq_len)
+    torch.cuda.synchronize()
+    o, l = out.double().cpu().numpy(), lse.double().cpu().numpy()
+    ro, rl = oracle.attend(inp)
+    assert_close(o, ro, tolerance(w), f"cascade {case}")
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(l), fin)
+    assert np.abs(l[fin] - rl[fin]).max() <= 1e-3 * max(1.0, np.abs(rl[fin]).max())
+
+
 # -------------------------------------------------------- bit-exact indexing
 
 @pytest.mark.parametrize("index", [0, 1, 4])
