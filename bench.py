@@ -308,6 +308,94 @@ def bench_verify(mla, args):
     print(json.dumps(line), flush=True)
 
 
+def bench_project(mla, args):
+    """The absorbed per-head projections on either side of one decode step of
+    the chosen workload: q_abs = W_UK^T q_nope (d_nope 128 -> d_latent) before
+    it and W_UV o (d_latent -> d_v 128) after it, for B*T token rows and all
+    heads, with random synthetic bf16 weights.  At decode batch sizes both are
+    weight-streaming: the roofline is HBM unless the flops take longer at the
+    bf16 MFMA peak."""
+    w = next(x for x in synth.WORKLOADS if x.name == args.workload)
+    M, G, Dc = w.batch * w.q_len, w.heads, w.d_latent
+    sides = [("query", synth.PROJ_D_NOPE, Dc), ("value", Dc, synth.PROJ_D_V)]
+    import ctypes
+    lib = mla.library()
+    P_ = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = sum(2 * (M * G * K + G * N * K + M * G * N) for _, K, N in sides)
+    flops = sum(2 * M * G * K * N for _, K, N in sides)
+    # In a model, each layer's weights come back only after every other layer's:
+    # rotate through enough copies that one pass exceeds twice the last-level
+    # cache, so that every launch streams its operands from HBM.
+    copies = int(max(1, -(-2 * LLC_BYTES // nbytes)))
+    host, sets = [], []
+    for i, (name, K, N) in enumerate(sides):
+        xb, wb = synth.make_projection_inputs(M, G, K, N, seed=31 + i)
+        host.append((xb, wb))
+        x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+        wt = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).cuda()
+        sets.append([(x.clone(), wt.clone(), torch.empty((M, G, N), dtype=torch.bfloat16, device="cuda"))
+                     for _ in range(copies)])
+    calls = [[(M, G, K, N, P_(sets[i][c][0]), P_(sets[i][c][1]), mla.MLA_DTYPE_BF16, P_(sets[i][c][2]), stream)
+              for i, (_, K, N) in enumerate(sides)] for c in range(copies)]
+    for step in range(args.warmup):
+        for c in calls[step % copies]:
+            if lib.mla_project(*c):
+                raise RuntimeError("mla_project failed")
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for step, (e0, e1) in enumerate(evs):
+        e0.record()
+        for c in calls[(args.warmup + step) % copies]:
+            lib.mla_project(*c)
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))  # both launches
+    t_hbm, t_mfma = nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(nbytes / (k_ms / 1e3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops / (k_ms / 1e3) / 1e12, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof.update({"frac": round(roof["achieved"] / roof["peak"], 4), "traffic": None,
+                 "kernel": "mla_project_kernel (query and value side)", "per_step_algorithmic_bytes": nbytes,
+                 "per_step_flops": flops, "kernels_ms_per_step": round(k_ms, 5)})
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+
+        def run_oracle(rows):
+            for xb, wb in host:
+                oracle.project(synth.bf16_bits_to_f32(xb[:rows]).astype(np.float64),
+                               synth.bf16_bits_to_f32(wb).astype(np.float64))
+        t1 = time.perf_counter()
+        run_oracle(1)                               # calibrate, then take rows for ~the budget
+        per_row = time.perf_counter() - t1
+        sub = int(max(1, min(M, args.cpu_budget / max(per_row, 1e-6))))
+        t1 = time.perf_counter()
+        run_oracle(sub)
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(sub / dt, 2), "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+               "sample": f"{sub} of {M} token rows through both projections, fp64 C oracle, {dt:.2f} s"}
+    line = {
+        "metric": "absorbed MLA projections (W_UK^T q_nope, W_UV o), tokens/s (1 MI355X)",
+        "value": round(M / (k_ms / 1e3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*0.5 activations, N(0,1)/sqrt(k) weights, bf16)",
+        "config": {"workload": f"project_{w.name}", "token_rows": M, "heads": G, "d_nope": synth.PROJ_D_NOPE,
+                   "d_latent": Dc, "d_v": synth.PROJ_D_V, "operand_copies_rotated": copies,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,9 +414,10 @@ def main():
     ap.add_argument("--pmc-out", metavar="FILE", help="where --pmc-summary writes its summary")
     ap.add_argument("--cascade", action="store_true",
                     help="decode with mla_decode_cascade over the workload's shared prefix")
-    ap.add_argument("--op", choices=("decode", "append", "verify"), default="decode",
+    ap.add_argument("--op", choices=("decode", "append", "verify", "project"), default="decode",
                     help="decode (the default hot path), the paged KV append with FP8 packing, "
-                         "or the greedy verification of speculative drafts")
+                         "the greedy verification of speculative drafts, or the absorbed "
+                         "projections around one decode step of --workload")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, args.workload, args.calib_copy_mib or 1024,
@@ -343,6 +432,9 @@ def main():
     torch.cuda.set_device(0)
     if args.op == "append":
         bench_append(mla, args)
+        return
+    if args.op == "project":
+        bench_project(mla, args)
         return
     if args.op == "verify":
         bench_verify(mla, args)

@@ -285,6 +285,31 @@ int mla_verify_greedy(int32_t batch, int32_t num_positions, int32_t vocab, const
                       int32_t* out_tokens, hipStream_t stream);
 
 /*
+ * Per-head projection on either side of the latent attention: the absorbed
+ * up-projections of MLA (TokenSpeed code-audit article, MLA entry: keys and
+ * values are stored as one low-rank latent per token and decompressed per
+ * head by up-projection matrices, which folding into the query and the
+ * output avoids).  For every row m and head g
+ *
+ *   out[m, g, n] = sum_k w[g, n, k] * x[m, g, k]      (fp32 accumulation)
+ *
+ *   x    [rows, heads, in_dim]  BF16, device (row-major, in_dim contiguous)
+ *   w    [heads, out_dim, in_dim] BF16, device (in_dim contiguous)
+ *   out  [rows, heads, out_dim] out_dtype (F32 or BF16, nearest-even), device
+ * Query side: x = q_nope [B*T, H, d_nope] and w[h] = W_UK[h] transposed,
+ * stored [H, d_latent, d_nope] once at weight-load time; out is q_absorbed
+ * [B*T, H, d_latent], the layout mla_decode() reads.  Value side: x = the
+ * attention output o [B*T, H, d_latent] and w = W_UV [H, d_v, d_latent] as
+ * is; out is the per-head value [B*T, H, d_v] that feeds the output
+ * projection.  in_dim and out_dim must be multiples of 8 (else
+ * MLA_ERR_UNSUPPORTED) and x, w, out 16-byte aligned (else
+ * MLA_ERR_INVALID_ARG); rows = 0 enqueues nothing.  out must not overlap x or w.
+ */
+int mla_project(int32_t rows, int32_t heads, int32_t in_dim, int32_t out_dim, const void* x,
+                const void* w, int32_t out_dtype, void* out, hipStream_t stream);
+
+/*
+ * Test hook for the page-table loader/*
  * Test hook for the page-table loader: copies, bit for bit, the stored rows
  * of logical token tok[i] of request req[i] (i < n) into out [n, Dc+Dr]
  * (kv_dtype elements), resolving pages with the same device address routine

@@ -25,7 +25,7 @@ EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_decode_spl
            "mla_combine", "mla_balanced_workgroups",
            "mla_decode_split_balanced", "mla_combine_balanced", "mla_cascade_workspace_size",
            "mla_decode_cascade", "mla_append_kv", "mla_verify_greedy",
-           "mla_gather_rows",
+           "mla_project", "mla_gather_rows",
            "mla_check_tables", "mla_status_string")
 
 BALANCED_ROWS = 128  # rows per unit of the balanced work list
@@ -72,6 +72,7 @@ def library():
     lib.mla_decode_cascade.argtypes = [PP, P, P, P, P, P, P, ctypes.c_float, i32, P, P, P, sz, P]
     lib.mla_append_kv.argtypes = [PP, P, i32, P, P, P, P, P]
     lib.mla_verify_greedy.argtypes = [i32, i32, i32, P, i32, P, P, P, P, P]
+    lib.mla_project.argtypes = [i32, i32, i32, i32, P, P, i32, P, P]
     lib.mla_gather_rows.argtypes = [PP, P, P, i32, P, P, P, P]
     lib.mla_check_tables.argtypes = [PP, P, P]
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -357,6 +358,29 @@ def verify_greedy(logits, draft=None):
                                        _ptr(draft) if T > 1 else None, _ptr(am), _ptr(n), _ptr(out),
                                        _stream()), "mla_verify_greedy")
     return am, n, out
+
+
+def project(x, w, *, out_dtype=torch.bfloat16, out=None):
+    """Per-head projection through ``mla_project``: x [M, G, K] and w [G, N, K]
+    bfloat16 -> out [M, G, N] with out[m, g, n] = sum_k w[g, n, k] x[m, g, k].
+    Query side: x = q_nope, w = W_UK transposed per head ([G, d_latent, d_nope]);
+    value side: x = the attention output, w = W_UV ([G, d_v, d_latent])."""
+    dev = x.device
+    _require(x, "x", dev, dtype=torch.bfloat16, ndim=3)
+    _require(w, "w", dev, dtype=torch.bfloat16, ndim=3)
+    M, G, K = x.shape
+    if w.shape[0] != G or w.shape[2] != K:
+        raise ValueError(f"w must be [{G}, N, {K}], got {tuple(w.shape)}")
+    N = w.shape[1]
+    if out is None:
+        out = torch.empty((M, G, N), dtype=out_dtype, device=dev)
+    else:
+        _require(out, "out", dev, dtype=out_dtype, ndim=3)
+        if tuple(out.shape) != (M, G, N):
+            raise ValueError("out must be [M, G, N]")
+    _check(library().mla_project(M, G, K, N, _ptr(x), _ptr(w), _dtype_code(out), _ptr(out), _stream()),
+           "mla_project")
+    return out
 
 
 def gather_rows(kv_pages, page_table, req, tok, *, d_latent, d_rope=None):

@@ -475,6 +475,23 @@ int mla_verify_greedy(int32_t batch, int32_t num_positions, int32_t vocab, const
              : MLA_ERR_HIP;
 }
 
+int mla_project(int32_t rows, int32_t heads, int32_t in_dim, int32_t out_dim, const void* x,
+                const void* w, int32_t out_dtype, void* out, hipStream_t stream) {
+  if (rows < 0 || heads < 1 || in_dim < 8 || out_dim < 8) return MLA_ERR_INVALID_ARG;
+  if (in_dim % 8 != 0 || out_dim % 8 != 0) return MLA_ERR_UNSUPPORTED;
+  if (out_dtype != MLA_DTYPE_F32 && out_dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  const int64_t tiles = (int64_t)heads * ((rows + 31) / 32) * ((out_dim + 63) / 64);
+  if ((int64_t)rows * heads * in_dim > (int64_t)1 << 40 || (int64_t)rows * heads * out_dim > (int64_t)1 << 40 ||
+      (int64_t)heads * out_dim * in_dim > (int64_t)1 << 40 || tiles > (int64_t)1 << 28)
+    return MLA_ERR_INVALID_ARG;
+  if (rows == 0) return MLA_OK;
+  if (!x || !w || !out) return MLA_ERR_INVALID_ARG;
+  if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)out) % 16 != 0) return MLA_ERR_INVALID_ARG;
+  return mla::launch_project(rows, heads, in_dim, out_dim, x, w, out_dtype, out, stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
 int mla_gather_rows(const mla_problem* problem, const void* kv_pages, const int32_t* page_table,
                     int32_t n, const int32_t* req, const int32_t* tok, void* out,
                     hipStream_t stream) {

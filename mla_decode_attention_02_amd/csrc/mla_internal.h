@@ -32,13 +32,13 @@ struct SplitParams {
   // the 32-token tiles of all units (request, group of kBalancedRows rows)
   // are cut into NB equal contiguous ranges, one per workgroup.
   int32_t NB;
-  int32_t* tile_prefix;
+  int32_t* tile_prefix;        // [B * groups + 1] exclusive prefix of tiles per unit,
+                               // written by workgroup 0 for the merge
   // Cascade (uniform chunks only; Sp == 0 disables it): chunks 0..Sp-1 split
   // the first prefix_len tokens (a prefix every request shares) with the same
   // page-aligned bounds for all requests, chunks Sp..S-1 split [prefix_len, L_b).
   int32_t Sp;
-  int32_t prefix_len;        // [B * groups + 1] exclusive prefix of tiles per unit,
-                               // written by workgroup 0 for the merge
+  int32_t prefix_len;
 };
 
 // Rows per unit of the balanced work list (the MFMA kernels' workgroup rows).
@@ -77,6 +77,10 @@ hipError_t launch_append(int32_t B, int32_t T, int32_t D, int32_t P, int32_t MP,
 hipError_t launch_verify(int32_t B, int32_t T, int32_t V, int32_t dtype, const void* logits,
                          const int32_t* draft, int32_t* argmax, int32_t* accept_len, int32_t* out,
                          hipStream_t stream);
+
+// Per-head projection (see mla_project); arguments validated, bf16 x and w.
+hipError_t launch_project(int32_t M, int32_t G, int32_t K, int32_t N, const void* x, const void* w,
+                          int32_t out_dtype, void* out, hipStream_t stream);
 
 hipError_t launch_gather(int32_t Dc, int32_t Dr, int32_t P, int32_t MP, int32_t kv_dtype,
                          const void* kv, const int32_t* page_table, int32_t n,

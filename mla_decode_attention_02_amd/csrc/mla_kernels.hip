@@ -1447,6 +1447,112 @@ mla_verify_kernel(int T, int V, int dtype, const void* __restrict__ logits, cons
 }
 
 // ------------------------------------------------------------ gather hook
+// ---------------------------------------------------------------------------
+// Per-head projection on either side of the latent attention (the absorbed
+// projections of MLA: q_abs = W_UK^T q_nope forms the query, W_UV o the
+// head's value output):  out[m][g][n] = sum_k w[g][n][k] * x[m][g][k].
+//
+// It is a batch of G small GEMMs that at decode batch sizes streams its
+// weights once from HBM (about 73 flops per byte at M = 64, well under the
+// chip's bf16 ridge), so the design goal is bytes in flight, not MFMA rate.
+// One workgroup owns a 32 (m) x 64 (n) output tile of one head.  The k range
+// is cut into 32-wide chunks dealt round-robin to the four waves, so even a
+// short k loop (k = 128: one chunk per wave) keeps every wave loading; each
+// wave issues all loads of up to four chunks before its first MFMA.  Operands
+// go from HBM straight into the MFMA layout: both are k-contiguous, so lane
+// (i, half) reads 16 contiguous bytes of row i per MFMA step.  The four
+// partial tiles are summed through LDS, which also turns the accumulator
+// layout into 16-byte row stores.  Tiles are numbered head-major and dealt in
+// contiguous ranges per XCD, so the tiles that share a head's x rows and
+// weight rows share one L2.
+constexpr int kPjWaves = 4, kPjTileM = 32, kPjTileN = 64, kPjChunk = 32, kPjGroup = 4;
+
+__device__ __forceinline__ bf16x8 pj_load(const __bf16* row, int k, int K, bool valid) {
+  if (valid && k < K) return *(const bf16x8*)(row + k);
+  return bf16x8{};
+}
+
+template <typename OutT>
+__global__ void __launch_bounds__(64 * kPjWaves)
+mla_project_kernel(int M, int G, int K, int N, const __bf16* __restrict__ x, const __bf16* __restrict__ w,
+                   OutT* __restrict__ out, int tiles_m, int tiles_n, int per_xcd, int tiles) {
+  constexpr int kPitch = kPjTileN + 4;  // floats; the pad spreads the row-scattered writes
+  __shared__ float red[kPjWaves][kPjTileM][kPitch];
+  const int bid = blockIdx.x;
+  const int u = (bid & 7) * per_xcd + (bid >> 3);
+  if (u >= tiles) return;  // whole workgroup, before any barrier
+  const int per_head = tiles_m * tiles_n;
+  const int g = u / per_head;
+  const int mt = (u - g * per_head) / tiles_n;
+  const int nt = u - g * per_head - mt * tiles_n;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 31, half = lane >> 5;
+  // MFMA operand A = weight rows (output columns n), B = x rows (output rows m)
+  const int m = mt * kPjTileM + i;
+  const int n0 = nt * kPjTileN + i, n1 = n0 + 32;
+  const bool vm = m < M, vn0 = n0 < N, vn1 = n1 < N;
+  const __bf16* xr = x + ((int64_t)(vm ? m : 0) * G + g) * K + 8 * half;
+  const __bf16* w0 = w + ((int64_t)g * N + (vn0 ? n0 : 0)) * K + 8 * half;
+  const __bf16* w1 = w + ((int64_t)g * N + (vn1 ? n1 : 0)) * K + 8 * half;
+  const int Kh = K - 8 * half;  // a piece at k (relative to this lane's base) exists iff k < Kh
+  floatx16 acc0 = {}, acc1 = {};
+  const int nch = (K + kPjChunk - 1) / kPjChunk;
+  for (int c0 = wave; c0 < nch; c0 += kPjWaves * kPjGroup) {
+    bf16x8 xa[kPjGroup][2], wa[kPjGroup][2], wb[kPjGroup][2];
+#pragma unroll
+    for (int s = 0; s < kPjGroup; ++s)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int k = (c0 + kPjWaves * s) * kPjChunk + 16 * st;
+        xa[s][st] = pj_load(xr, k, Kh, vm);
+        wa[s][st] = pj_load(w0, k, Kh, vn0);
+        wb[s][st] = pj_load(w1, k, Kh, vn1);
+      }
+#pragma unroll
+    for (int s = 0; s < kPjGroup; ++s) {
+      if (c0 + kPjWaves * s >= nch) break;  // wave-uniform
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[s][st], xa[s][st], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[s][st], xa[s][st], acc1, 0, 0, 0);
+      }
+    }
+  }
+  // accumulator register r of lane (i, half) holds output row m = i and
+  // column n = 8 (r / 4) + 4 half + r % 4 (+ 32 for acc1)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int nl = 8 * q + 4 * half;
+    *(floatx4*)&red[wave][i][nl] = floatx4{acc0[4 * q], acc0[4 * q + 1], acc0[4 * q + 2], acc0[4 * q + 3]};
+    *(floatx4*)&red[wave][i][nl + 32] = floatx4{acc1[4 * q], acc1[4 * q + 1], acc1[4 * q + 2], acc1[4 * q + 3]};
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int ml = t >> 3, nl = 8 * (t & 7);
+  const int mo = mt * kPjTileM + ml, no = nt * kPjTileN + nl;
+  if (mo >= M || no >= N) return;  // N is a multiple of 8: a piece is all in or all out
+  floatx4 s0 = *(const floatx4*)&red[0][ml][nl], s1 = *(const floatx4*)&red[0][ml][nl + 4];
+#pragma unroll
+  for (int v = 1; v < kPjWaves; ++v) {
+    s0 += *(const floatx4*)&red[v][ml][nl];
+    s1 += *(const floatx4*)&red[v][ml][nl + 4];
+  }
+  OutT* dst = out + ((int64_t)mo * G + g) * N + no;
+  if constexpr (sizeof(OutT) == 4) {
+    *(floatx4*)dst = s0;
+    *(floatx4*)(dst + 4) = s1;
+  } else {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] = (__bf16)s0[e];
+      o[4 + e] = (__bf16)s1[e];
+    }
+    *(bf16x8*)dst = o;
+  }
+}
+
 __global__ void mla_gather_kernel(int D, int elt, int P, int MP, const char* __restrict__ kv,
                                   const int32_t* __restrict__ page_table, int n,
                                   const int32_t* __restrict__ req, const int32_t* __restrict__ tok,
@@ -1550,6 +1656,22 @@ hipError_t launch_verify(int32_t B, int32_t T, int32_t V, int32_t dtype, const v
   if (B == 0) return hipSuccess;
   hipLaunchKernelGGL(mla_verify_kernel, dim3((unsigned)B), dim3(1024), 0, stream, T, V, dtype, logits, draft,
                      argmax, accept_len, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_project(int32_t M, int32_t G, int32_t K, int32_t N, const void* x, const void* w,
+                          int32_t out_dtype, void* out, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int tiles_m = (M + kPjTileM - 1) / kPjTileM, tiles_n = (N + kPjTileN - 1) / kPjTileN;
+  const int64_t tiles = (int64_t)G * tiles_m * tiles_n;
+  const int64_t per_xcd = (tiles + 7) / 8;
+  const dim3 grid((unsigned)(8 * per_xcd)), block(64 * kPjWaves);
+  if (out_dtype == kF32)
+    hipLaunchKernelGGL(mla_project_kernel<float>, grid, block, 0, stream, M, G, K, N, (const __bf16*)x,
+                       (const __bf16*)w, (float*)out, tiles_m, tiles_n, (int)per_xcd, (int)tiles);
+  else
+    hipLaunchKernelGGL(mla_project_kernel<__bf16>, grid, block, 0, stream, M, G, K, N, (const __bf16*)x,
+                       (const __bf16*)w, (__bf16*)out, tiles_m, tiles_n, (int)per_xcd, (int)tiles);
   return hipGetLastError();
 }
 

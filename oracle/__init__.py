@@ -59,6 +59,8 @@ def load(rebuild=False):
     lib.orc_e4m3_value.restype = ctypes.c_double
     lib.orc_append_rows.argtypes = [i32, i32, i32, P, P, i32, i32, i32, P, i32, P, P]
     lib.orc_append_rows.restype = ctypes.c_int
+    lib.orc_project.argtypes = [i32, i32, i32, i32, P, P, P]
+    lib.orc_project.restype = ctypes.c_int
     lib.orc_verify_greedy.argtypes = [i32, i32, i32, P, P, P, P, P]
     lib.orc_verify_greedy.restype = ctypes.c_int
     lib.orc_e4m3_code.argtypes = [ctypes.c_float]
@@ -230,3 +232,16 @@ def verify_greedy(logits, draft):
     _check(load().orc_verify_greedy(B, T, V, _ptr(lg), _ptr(d) if d.size else None, _ptr(am), _ptr(n),
                                     _ptr(out)), "orc_verify_greedy")
     return am, n, out
+
+
+def project(x, w):
+    """Per-head projection out[m, g, n] = sum_k w[g, n, k] x[m, g, k] in fp64
+    (see orc_project).  x [M, G, K], w [G, N, K] (any real dtype, exact values)."""
+    xx = np.ascontiguousarray(x, dtype=np.float64)
+    ww = np.ascontiguousarray(w, dtype=np.float64)
+    M, G, K = xx.shape
+    G2, N, K2 = ww.shape
+    assert G2 == G and K2 == K
+    out = np.zeros((M, G, N), dtype=np.float64)
+    _check(load().orc_project(M, G, K, N, _ptr(xx), _ptr(ww), _ptr(out)), "orc_project")
+    return out

@@ -472,6 +472,33 @@ int orc_verify_greedy(int32_t B, int32_t T, int32_t V, const double* logits, con
   return ORC_OK;
 }
 
+/*
+ * Per-head projection on either side of the latent attention (the absorbed
+ * projections of the code-audit article's MLA entry): for row m and head g,
+ *   out[m][g][n] = sum_k W[g][n][k] * x[m][g][k]
+ * in fp64, k in order.  With W[g] = W_UK^g transposed (d_latent x d_nope)
+ * and x = q_nope this forms the absorbed query q_abs = W_UK^T q_nope; with
+ * W[g] = W_UV^g (d_v x d_latent) and x = the attention output o it forms the
+ * head's value output W_UV o.  x: [M, G, K], W: [G, N, K], out: [M, G, N].
+ */
+int orc_project(int32_t M, int32_t G, int32_t K, int32_t N, const double* x, const double* w, double* out) {
+  if (M < 0 || G < 1 || K < 1 || N < 1 || !x || !w || !out) return ORC_BAD_ARG;
+#ifdef _OPENMP
+#pragma omp parallel for collapse(2) schedule(static)
+#endif
+  for (int m = 0; m < M; ++m)
+    for (int g = 0; g < G; ++g) {
+      const double* xr = x + ((size_t)m * G + g) * K;
+      for (int n = 0; n < N; ++n) {
+        const double* wr = w + ((size_t)g * N + n) * K;
+        double acc = 0.0;
+        for (int k = 0; k < K; ++k) acc += wr[k] * xr[k];
+        out[((size_t)m * G + g) * N + n] = acc;
+      }
+    }
+  return ORC_OK;
+}
+
 /* E4M3 code of one fp32 value (for pinning the encoder on its own). */
 uint8_t orc_e4m3_code(float q) { return e4m3_code_of(q); }
 uint16_t orc_bf16_bits(float v) { return bf16_bits_of(v); }

@@ -208,3 +208,21 @@ def make_inputs(w, seed=None, poison=True, seq_lens=None):
 def chunk_count_hint(w):
     """Number of page-aligned chunks a request of max length is cut into when splits are forced."""
     return w.num_splits
+
+
+# Shapes of the per-head projections on either side of the attention for the
+# DeepSeek-style workloads: d_nope = 128 (the score scale 1/sqrt(192) covers
+# 128 non-rope + 64 rope query dims) and d_v = d_nope.
+PROJ_D_NOPE = 128
+PROJ_D_V = 128
+
+
+def make_projection_inputs(M, G, K, N, seed, sigma_x=0.5):
+    """Seeded bf16 inputs of one per-head projection: x [M, G, K] ~ N(0,1) * sigma_x
+    and random synthetic weights w [G, N, K] ~ N(0,1) / sqrt(K), drawn in fp32
+    (x first, then w) and rounded once to bf16.  Returns (x_bits, w_bits) as
+    uint16 arrays of bf16 bit patterns."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((M, G, K), dtype=np.float32) * np.float32(sigma_x)).astype(np.float32)
+    w = (rng.standard_normal((G, N, K), dtype=np.float32) * np.float32(1.0 / math.sqrt(K))).astype(np.float32)
+    return f32_to_bf16_bits(x), f32_to_bf16_bits(w)

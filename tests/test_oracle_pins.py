@@ -622,3 +622,51 @@ def test_verify_acceptance_is_the_run_of_leading_matches(T):
         assert n[b] == k
         assert list(out[b, :k]) == list(draft[b, :k]) and out[b, k] == p[b, k]
         assert (out[b, k + 1:] == -1).all()
+
+
+# ---------------------------------------------------------------- projections
+
+@pytest.mark.parametrize("w", [tiny(), small_ds(q_len=2, causal=True, heads=4)], ids=["tiny", "ds_causal"])
+def test_projections_around_the_oracle_equal_expanded_mha(w):
+    """Query side: project(q_nope, W_UK^T per head) is the absorbed query (the
+    dyadic case makes it exact); value side: project(o, W_UV) equals attention
+    over decompressed keys and values, computed without any projection call."""
+    inp, W_UK, W_UV, q_nope = _absorbed_case(w, seed=11)
+    B, T, H = w.batch, w.q_len, w.heads
+    q_abs = oracle.project(q_nope.reshape(B * T, H, -1), W_UK.transpose(0, 2, 1))
+    assert np.array_equal(q_abs.reshape(B, T, H, -1), stored_values(inp, "q_abs"))
+    o, _ = oracle.attend(inp)
+    got = oracle.project(o.reshape(B * T, H, -1), W_UV).reshape(B, T, H, -1)
+    ref = _expanded_mha(inp, W_UK, W_UV, q_nope)
+    assert np.abs(got - ref).max() <= 1e-10 * np.abs(ref).max()
+
+
+def test_projection_one_hot_weights_pick_one_input_column():
+    """w[g] with a single 1 at (n_g, k_g), different per head, copies x[:, g, k_g]
+    to out[:, g, n_g] and leaves every other output zero (index roles)."""
+    M, G, K, N = 5, 3, 6, 6
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((M, G, K))
+    w = np.zeros((G, N, K))
+    picks = [(1, 4), (5, 0), (2, 3)]
+    for g, (n, k) in enumerate(picks):
+        w[g, n, k] = 1.0
+    out = oracle.project(x, w)
+    expect = np.zeros((M, G, N))
+    for g, (n, k) in enumerate(picks):
+        expect[:, g, n] = x[:, g, k]
+    assert np.array_equal(out, expect)
+
+
+def test_projection_matches_matmul_per_head():
+    M, G, K, N = 7, 4, 24, 16
+    xb, wb = synth.make_projection_inputs(M, G, K, N, seed=5)
+    x, w = synth.bf16_bits_to_f32(xb).astype(np.float64), synth.bf16_bits_to_f32(wb).astype(np.float64)
+    out = oracle.project(x, w)
+    for g in range(G):
+        ref = x[:, g, :] @ w[g].T
+        assert np.abs(out[:, g, :] - ref).max() <= 1e-13 * np.abs(ref).max()
+
+
+def test_projection_of_no_rows():
+    assert oracle.project(np.zeros((0, 2, 8)), np.ones((2, 3, 8))).shape == (0, 2, 3)
