@@ -1458,21 +1458,23 @@ mla_verify_kernel(int T, int V, int dtype, const void* __restrict__ logits, cons
 // One workgroup owns a 32 (m) x 64 (n) output tile of one head.  The k range
 // is cut into 32-wide chunks dealt round-robin to the four waves, so even a
 // short k loop (k = 128: one chunk per wave) keeps every wave loading; each
-// wave issues all loads of up to four chunks before its first MFMA.  Operands
+// wave issues all loads of its chunks (up to four) before its first MFMA, and
+// the register budget follows the chunks a wave holds (more resident
+// workgroups when k is short).  Operands
 // go from HBM straight into the MFMA layout: both are k-contiguous, so lane
 // (i, half) reads 16 contiguous bytes of row i per MFMA step.  The four
 // partial tiles are summed through LDS, which also turns the accumulator
 // layout into 16-byte row stores.  Tiles are numbered head-major and dealt in
 // contiguous ranges per XCD, so the tiles that share a head's x rows and
 // weight rows share one L2.
-constexpr int kPjWaves = 4, kPjTileM = 32, kPjTileN = 64, kPjChunk = 32, kPjGroup = 4;
+constexpr int kPjWaves = 4, kPjTileM = 32, kPjTileN = 64, kPjChunk = 32;
 
 __device__ __forceinline__ bf16x8 pj_load(const __bf16* row, int k, int K, bool valid) {
   if (valid && k < K) return *(const bf16x8*)(row + k);
   return bf16x8{};
 }
 
-template <typename OutT>
+template <typename OutT, int kPjGroup>
 __global__ void __launch_bounds__(64 * kPjWaves)
 mla_project_kernel(int M, int G, int K, int N, const __bf16* __restrict__ x, const __bf16* __restrict__ w,
                    OutT* __restrict__ out, int tiles_m, int tiles_n, int per_xcd, int tiles) {
@@ -1550,6 +1552,122 @@ mla_project_kernel(int M, int G, int K, int N, const __bf16* __restrict__ x, con
       o[4 + e] = (__bf16)s1[e];
     }
     *(bf16x8*)dst = o;
+  }
+}
+
+// Staged form for k a multiple of 64: a 64 (m) x 64 (n) output tile per
+// workgroup, its operands streamed through a ring of LDS stages by direct
+// HBM -> LDS loads.  A stage holds 64 k of the tile's 64 x rows and 64 weight
+// rows (128 bytes of each row, 16 KB); each 64-lane load moves eight whole
+// 128-byte rows, so every request is a full cache line (the register-direct
+// form above reads 32 rows x 32 bytes per instruction).  In LDS, row r's
+// 16-byte column c sits at r * 128 + 16 (c ^ (r & 7)): the loads place it
+// there by permuting their source addresses within the row, and the MFMA
+// operand reads (32 rows, one logical column per half-wave) then hit eight
+// distinct 16-byte bank groups per eight lanes.  Waves form a 2 x 2 grid of
+// 32 x 32 MFMA tiles.  Rows past M or N load a clamped in-range row whose
+// results are never stored.
+constexpr int kPsTile = 64, kPsStageBytes = 2 * kPsTile * 128;
+
+template <typename OutT, int STAGES>
+__global__ void __launch_bounds__(256)
+mla_project_staged(int M, int G, int K, int N, const __bf16* __restrict__ x, const __bf16* __restrict__ w,
+                   OutT* __restrict__ out, int tiles_m, int tiles_n, int per_xcd, int tiles) {
+  extern __shared__ __attribute__((aligned(1024))) char pj_smem_raw[];
+  LDS_AS char* smem = (LDS_AS char*)pj_smem_raw;
+  const int bid = blockIdx.x;
+  const int u = (bid & 7) * per_xcd + (bid >> 3);
+  if (u >= tiles) return;  // whole workgroup, before any barrier
+  const int per_head = tiles_m * tiles_n;
+  const int g = u / per_head;
+  const int mt = (u - g * per_head) / tiles_n;
+  const int nt = u - g * per_head - mt * tiles_n;
+  const int m0 = mt * kPsTile, n0 = nt * kPsTile;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // loads: waves 0, 1 fill the x rows, waves 2, 3 the weight rows, four
+  // 8-row groups each; lane L takes row 8 j + L / 8, physical column L % 8
+  const bool xside = wave < 2;
+  const int lr = lane >> 3, lc = (lane & 7) ^ lr;  // (8 j + lr) & 7 == lr
+  const char* gbase;
+  int64_t gstep;  // bytes per stage along k
+  uint32_t voff[4];
+  if (xside) {
+    gbase = (const char*)(x + ((int64_t)m0 * G + g) * K);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * (4 * wave + q) + lr;
+      const int rm = (m0 + r < M ? r : M - 1 - m0);
+      voff[q] = (uint32_t)((int64_t)rm * G * K * 2 + 16 * lc);
+    }
+  } else {
+    gbase = (const char*)(w + ((int64_t)g * N + n0) * K);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * (4 * (wave - 2) + q) + lr;
+      const int rn = (n0 + r < N ? r : N - 1 - n0);
+      voff[q] = (uint32_t)((int64_t)rn * K * 2 + 16 * lc);
+    }
+  }
+  gstep = 128;
+  const int nst = K / 64;
+  auto issue = [&](int t) {
+    LDS_AS char* slot = smem + (t % STAGES) * kPsStageBytes;
+    const char* gb = gbase + (int64_t)t * gstep;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lds_dma16(gb, voff[q], lds_addr(slot + 1024 * (4 * wave + q)));
+  };
+  // all STAGES slots are filled up front; after that, step t refills the slot
+  // that step t - 1 read
+#pragma unroll
+  for (int t = 0; t < STAGES; ++t)
+    if (t < nst) issue(t);
+  const int i = lane & 31, h = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+  // operand rows: A = weight row 32 wn + i, B = x row 32 wm + i (same & 7 = i & 7)
+  const int ra = 8192 + (32 * wn + i) * 128, rb = (32 * wm + i) * 128;
+  floatx16 acc = {};
+  for (int t = 0; t < nst; ++t) {
+    // stages issued so far: min(nst, STAGES) at t = 0, min(nst, t + STAGES - 1) after
+    const int issued = t == 0 ? STAGES : t + STAGES - 1;
+    const int ahead = (issued < nst ? issued : nst) - 1 - t;
+    wait_ahead<4>(ahead);
+    __syncthreads();  // stage t is in LDS for every wave; slot (t - 1) % STAGES is free
+    if (t >= 1 && t + STAGES - 1 < nst) issue(t + STAGES - 1);
+    const LDS_AS char* slot = smem + (t % STAGES) * kPsStageBytes;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int col = 16 * ((2 * s + h) ^ (i & 7));
+      const bf16x8 a = *(const LDS_AS bf16x8*)(slot + ra + col);
+      const bf16x8 b = *(const LDS_AS bf16x8*)(slot + rb + col);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+  }
+  // D[n][m]: register r of lane (i, h) holds n = 32 wn + 8 (r / 4) + 4 h + r % 4,
+  // m = 32 wm + i.  Staged as [m][n] OutT rows (pitch + 16 bytes), then stored
+  // as 16-byte pieces of whole rows.
+  constexpr int kRowB = kPsTile * (int)sizeof(OutT), kPitchB = kRowB + 16;
+  static_assert(kPsTile * kPitchB <= STAGES * kPsStageBytes, "output staging fits the stages");
+  __syncthreads();  // every wave is done with the stages
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int nl = 32 * wn + 8 * q + 4 * h;
+    LDS_AS char* dst = smem + (32 * wm + i) * kPitchB + nl * (int)sizeof(OutT);
+    if constexpr (sizeof(OutT) == 4) {
+      *(LDS_AS floatx4*)dst = floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    } else {
+      *(LDS_AS bf16x4*)dst = bf16x4{(__bf16)acc[4 * q], (__bf16)acc[4 * q + 1], (__bf16)acc[4 * q + 2],
+                                    (__bf16)acc[4 * q + 3]};
+    }
+  }
+  __syncthreads();
+  constexpr int kPieces = kPsTile * kRowB / 16, kPerRow = kRowB / 16;
+#pragma unroll
+  for (int e = threadIdx.x; e < kPieces; e += 256) {
+    const int ml = e / kPerRow, pc = e - ml * kPerRow;
+    const int mo = m0 + ml, no = n0 + pc * (16 / (int)sizeof(OutT));
+    if (mo < M && no < N)  // N is a multiple of 8: a piece is all in or all out
+      *(uintx4*)(out + ((int64_t)mo * G + g) * N + no) = *(const LDS_AS uintx4*)(smem + ml * kPitchB + 16 * pc);
   }
 }
 
@@ -1659,6 +1777,29 @@ hipError_t launch_verify(int32_t B, int32_t T, int32_t V, int32_t dtype, const v
   return hipGetLastError();
 }
 
+template <int S>
+hipError_t launch_staged(dim3 grid, hipStream_t stream, int M, int G, int K, int N, const void* x, const void* w,
+                         int32_t out_dtype, void* out, int tm, int tn, int64_t px, int64_t tl) {
+  const size_t lds = (size_t)S * kPsStageBytes;
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    const hipError_t e1 = hipFuncSetAttribute((const void*)mla_project_staged<float, S>,
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e2 = hipFuncSetAttribute((const void*)mla_project_staged<__bf16, S>,
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    attr_err = e1 != hipSuccess ? e1 : e2;
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  if (out_dtype == kF32)
+    hipLaunchKernelGGL((mla_project_staged<float, S>), grid, dim3(256), lds, stream, M, G, K, N, (const __bf16*)x,
+                       (const __bf16*)w, (float*)out, tm, tn, (int)px, (int)tl);
+  else
+    hipLaunchKernelGGL((mla_project_staged<__bf16, S>), grid, dim3(256), lds, stream, M, G, K, N, (const __bf16*)x,
+                       (const __bf16*)w, (__bf16*)out, tm, tn, (int)px, (int)tl);
+  return hipGetLastError();
+}
+
 hipError_t launch_project(int32_t M, int32_t G, int32_t K, int32_t N, const void* x, const void* w,
                           int32_t out_dtype, void* out, hipStream_t stream) {
   if (M == 0) return hipSuccess;
@@ -1666,12 +1807,25 @@ hipError_t launch_project(int32_t M, int32_t G, int32_t K, int32_t N, const void
   const int64_t tiles = (int64_t)G * tiles_m * tiles_n;
   const int64_t per_xcd = (tiles + 7) / 8;
   const dim3 grid((unsigned)(8 * per_xcd)), block(64 * kPjWaves);
-  if (out_dtype == kF32)
-    hipLaunchKernelGGL(mla_project_kernel<float>, grid, block, 0, stream, M, G, K, N, (const __bf16*)x,
-                       (const __bf16*)w, (float*)out, tiles_m, tiles_n, (int)per_xcd, (int)tiles);
-  else
-    hipLaunchKernelGGL(mla_project_kernel<__bf16>, grid, block, 0, stream, M, G, K, N, (const __bf16*)x,
-                       (const __bf16*)w, (__bf16*)out, tiles_m, tiles_n, (int)per_xcd, (int)tiles);
+  // staged form: k a multiple of 64, and every row offset within a tile's
+  // 64 rows fits the loads' 32-bit offsets
+  if (K % 64 == 0 && (int64_t)kPsTile * G * K * 2 < ((int64_t)1 << 31)) {
+    const int tm = (M + kPsTile - 1) / kPsTile, tn = (N + kPsTile - 1) / kPsTile;
+    const int64_t tl = (int64_t)G * tm * tn, px = (tl + 7) / 8;
+    const dim3 g2((unsigned)(8 * px));
+    // two stages hold all of k <= 128 (more resident workgroups); four otherwise
+    if (K <= 128) return launch_staged<2>(g2, stream, M, G, K, N, x, w, out_dtype, out, tm, tn, px, tl);
+    return launch_staged<4>(g2, stream, M, G, K, N, x, w, out_dtype, out, tm, tn, px, tl);
+  }
+  const int nch = (K + kPjChunk - 1) / kPjChunk, per_wave = (nch + kPjWaves - 1) / kPjWaves;
+#define PJ_LAUNCH(T, GR) hipLaunchKernelGGL((mla_project_kernel<T, GR>), grid, block, 0, stream, M, G, K, N, (const __bf16*)x, \
+                       (const __bf16*)w, (T*)out, tiles_m, tiles_n, (int)per_xcd, (int)tiles)
+  if (out_dtype == kF32) {
+    if (per_wave <= 1) PJ_LAUNCH(float, 1); else if (per_wave <= 2) PJ_LAUNCH(float, 2); else PJ_LAUNCH(float, 4);
+  } else {
+    if (per_wave <= 1) PJ_LAUNCH(__bf16, 1); else if (per_wave <= 2) PJ_LAUNCH(__bf16, 2); else PJ_LAUNCH(__bf16, 4);
+  }
+#undef PJ_LAUNCH
   return hipGetLastError();
 }
 

@@ -55,7 +55,8 @@ def _check(got, x, w, rows, out_dtype):
 
 CASES = [
     # (M, G, K, N): ragged m and n tiles, k = 8 (one piece), k with a half-chunk
-    # tail, k shorter than one chunk per wave, both DeepSeek-side k/n roles
+    # tail, k shorter than one chunk per wave, both DeepSeek-side k/n roles;
+    # k not a multiple of 64 takes the register-direct form
     (5, 3, 64, 72),
     (37, 4, 128, 512),
     (33, 2, 512, 128),
@@ -63,6 +64,9 @@ CASES = [
     (70, 3, 520, 40),
     (32, 5, 40, 64),
     (64, 2, 1056, 136),
+    # the staged form (k a multiple of 64): tails in m and n, n below one tile
+    (3, 2, 192, 8),
+    (130, 3, 640, 200),
 ]
 
 
