@@ -87,3 +87,15 @@ def test_append_decode_shaped_batch(mla):
     ref, ref_sc = kv.copy(), sc.copy()
     oracle.append_rows(x, pt, pos, ref, ref_sc, dst="fp8")
     assert got.tobytes() == ref.tobytes() and got_sc.tobytes() == ref_sc.tobytes()
+
+
+@pytest.mark.parametrize("B,T", [(3, 3), (1, 1), (2, 7)])
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+def test_append_fp8_partial_row_groups(mla, B, T, src):
+    """Row counts that leave the last group of rows per wavefront partly empty
+    (rows are packed several per wavefront); only the appended slots change."""
+    x, pt, pos, kv, sc = _case(53 + 7 * B + T, B=B, T=T, D=576, P=16, MP=6, NP=30, src=src, dst="fp8")
+    got, got_sc = _run(mla, x, pt, pos, kv.copy(), sc.copy(), src, "fp8")
+    ref, ref_sc = kv.copy(), sc.copy()
+    oracle.append_rows(x, pt, pos, ref, ref_sc, dst="fp8")
+    assert got.tobytes() == ref.tobytes() and got_sc.tobytes() == ref_sc.tobytes()
