@@ -145,3 +145,25 @@ def test_combine_argument_checks(mla):
     assert lib.mla_combine(1, 2, 4, 512, None, fake, 1, fake, None, None) == mla.MLA_ERR_INVALID_ARG
     assert lib.mla_combine(1, 2, 4, 512, fake, fake, 2, fake, None, None) == mla.MLA_ERR_UNSUPPORTED
     assert lib.mla_combine(0, 2, 4, 512, None, None, 1, None, None, None) == mla.MLA_OK
+
+
+def test_project_argument_checks(mla):
+    """mla_project validates shapes, dtypes, pointers and alignment on the host."""
+    lib = mla.library()
+    fake = ctypes.c_void_p(0x1000)                  # 16-byte aligned, never dereferenced
+    ok = (64, 128, 128, 512)
+    assert lib.mla_project(0, 128, 128, 512, None, None, mla.MLA_DTYPE_BF16, None, None) == mla.MLA_OK
+    for dims, rc in (((-1, 128, 128, 512), mla.MLA_ERR_INVALID_ARG),
+                     ((64, 0, 128, 512), mla.MLA_ERR_INVALID_ARG),
+                     ((64, 128, 4, 512), mla.MLA_ERR_INVALID_ARG),
+                     ((64, 128, 132, 512), mla.MLA_ERR_UNSUPPORTED),
+                     ((64, 128, 128, 516), mla.MLA_ERR_UNSUPPORTED)):
+        assert lib.mla_project(*dims, fake, fake, mla.MLA_DTYPE_BF16, fake, None) == rc, dims
+    assert lib.mla_project(*ok, fake, fake, mla.MLA_DTYPE_FP8_E4M3, fake, None) == mla.MLA_ERR_UNSUPPORTED
+    for i in range(3):
+        ptrs = [fake, fake, fake]
+        ptrs[i] = None
+        assert lib.mla_project(*ok, ptrs[0], ptrs[1], mla.MLA_DTYPE_BF16, ptrs[2], None) == mla.MLA_ERR_INVALID_ARG
+        ptrs = [fake, fake, fake]
+        ptrs[i] = ctypes.c_void_p(0x1008)            # 8-byte aligned only
+        assert lib.mla_project(*ok, ptrs[0], ptrs[1], mla.MLA_DTYPE_BF16, ptrs[2], None) == mla.MLA_ERR_INVALID_ARG
