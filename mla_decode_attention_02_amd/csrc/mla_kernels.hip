@@ -1567,12 +1567,18 @@ mla_project_kernel(int M, int G, int K, int N, const __bf16* __restrict__ x, con
 // distinct 16-byte bank groups per eight lanes.  Waves form a 2 x 2 grid of
 // 32 x 32 MFMA tiles.  Rows past M or N load a clamped in-range row whose
 // results are never stored.
-constexpr int kPsTile = 64, kPsStageBytes = 2 * kPsTile * 128;
+constexpr int kPsTileN = 64;
+template <int TM>
+constexpr int ps_stage_bytes() { return (TM + kPsTileN) * 128; }
 
-template <typename OutT, int STAGES>
+template <typename OutT, int STAGES, int TM>
 __global__ void __launch_bounds__(256)
 mla_project_staged(int M, int G, int K, int N, const __bf16* __restrict__ x, const __bf16* __restrict__ w,
                    OutT* __restrict__ out, int tiles_m, int tiles_n, int per_xcd, int tiles) {
+  static_assert(TM == 64 || TM == 128, "tile rows");
+  constexpr int kStage = ps_stage_bytes<TM>();
+  constexpr int kLoads = (TM + kPsTileN) / 32;  // 8-row loads per wave per stage
+  constexpr int kMt = TM / 64;                  // 32-row m subtiles per wave
   extern __shared__ __attribute__((aligned(1024))) char pj_smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)pj_smem_raw;
   const int bid = blockIdx.x;
@@ -1582,40 +1588,38 @@ mla_project_staged(int M, int G, int K, int N, const __bf16* __restrict__ x, con
   const int g = u / per_head;
   const int mt = (u - g * per_head) / tiles_n;
   const int nt = u - g * per_head - mt * tiles_n;
-  const int m0 = mt * kPsTile, n0 = nt * kPsTile;
+  const int m0 = mt * TM, n0 = nt * kPsTileN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // loads: waves 0, 1 fill the x rows, waves 2, 3 the weight rows, four
-  // 8-row groups each; lane L takes row 8 j + L / 8, physical column L % 8
-  const bool xside = wave < 2;
+  // Load j (0 <= j < (TM + 64) / 8) of a stage moves tile rows 8 j .. 8 j + 7:
+  // the TM x rows first, then the 64 weight rows; wave v issues loads
+  // kLoads v .. kLoads v + kLoads - 1.  Lane L takes row 8 j + L / 8, physical
+  // column L % 8.
   const int lr = lane >> 3, lc = (lane & 7) ^ lr;  // (8 j + lr) & 7 == lr
-  const char* gbase;
-  int64_t gstep;  // bytes per stage along k
-  uint32_t voff[4];
-  if (xside) {
-    gbase = (const char*)(x + ((int64_t)m0 * G + g) * K);
+  const char* xb = (const char*)(x + ((int64_t)m0 * G + g) * K);
+  const char* wb = (const char*)(w + ((int64_t)g * N + n0) * K);
+  uint32_t voff[kLoads];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 8 * (4 * wave + q) + lr;
+  for (int q = 0; q < kLoads; ++q) {
+    const int j = kLoads * wave + q;
+    if (j < TM / 8) {
+      const int r = 8 * j + lr;
       const int rm = (m0 + r < M ? r : M - 1 - m0);
       voff[q] = (uint32_t)((int64_t)rm * G * K * 2 + 16 * lc);
-    }
-  } else {
-    gbase = (const char*)(w + ((int64_t)g * N + n0) * K);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 8 * (4 * (wave - 2) + q) + lr;
+    } else {
+      const int r = 8 * (j - TM / 8) + lr;
       const int rn = (n0 + r < N ? r : N - 1 - n0);
       voff[q] = (uint32_t)((int64_t)rn * K * 2 + 16 * lc);
     }
   }
-  gstep = 128;
   const int nst = K / 64;
   auto issue = [&](int t) {
-    LDS_AS char* slot = smem + (t % STAGES) * kPsStageBytes;
-    const char* gb = gbase + (int64_t)t * gstep;
+    LDS_AS char* slot = smem + (t % STAGES) * kStage;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lds_dma16(gb, voff[q], lds_addr(slot + 1024 * (4 * wave + q)));
+    for (int q = 0; q < kLoads; ++q) {
+      const int j = kLoads * wave + q;
+      lds_dma16((j < TM / 8 ? xb : wb) + 128 * t, voff[q], lds_addr(slot + 1024 * j));
+    }
   };
   // all STAGES slots are filled up front; after that, step t refills the slot
   // that step t - 1 read
@@ -1624,44 +1628,53 @@ mla_project_staged(int M, int G, int K, int N, const __bf16* __restrict__ x, con
     if (t < nst) issue(t);
   const int i = lane & 31, h = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
-  // operand rows: A = weight row 32 wn + i, B = x row 32 wm + i (same & 7 = i & 7)
-  const int ra = 8192 + (32 * wn + i) * 128, rb = (32 * wm + i) * 128;
-  floatx16 acc = {};
+  // operand rows: A = weight row 32 wn + i, B = x rows TM / 2 wm + 32 mi + i
+  // (all equal to i modulo 8)
+  const int ra = TM * 128 + (32 * wn + i) * 128, rb = ((TM / 2) * wm + i) * 128;
+  floatx16 acc[kMt];
+#pragma unroll
+  for (int mi = 0; mi < kMt; ++mi) acc[mi] = floatx16{};
   for (int t = 0; t < nst; ++t) {
     // stages issued so far: min(nst, STAGES) at t = 0, min(nst, t + STAGES - 1) after
     const int issued = t == 0 ? STAGES : t + STAGES - 1;
     const int ahead = (issued < nst ? issued : nst) - 1 - t;
-    wait_ahead<4>(ahead);
+    wait_ahead<kLoads>(ahead);
     __syncthreads();  // stage t is in LDS for every wave; slot (t - 1) % STAGES is free
     if (t >= 1 && t + STAGES - 1 < nst) issue(t + STAGES - 1);
-    const LDS_AS char* slot = smem + (t % STAGES) * kPsStageBytes;
+    const LDS_AS char* slot = smem + (t % STAGES) * kStage;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int col = 16 * ((2 * s + h) ^ (i & 7));
       const bf16x8 a = *(const LDS_AS bf16x8*)(slot + ra + col);
-      const bf16x8 b = *(const LDS_AS bf16x8*)(slot + rb + col);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+#pragma unroll
+      for (int mi = 0; mi < kMt; ++mi) {
+        const bf16x8 b = *(const LDS_AS bf16x8*)(slot + rb + 32 * 128 * mi + col);
+        acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[mi], 0, 0, 0);
+      }
     }
   }
   // D[n][m]: register r of lane (i, h) holds n = 32 wn + 8 (r / 4) + 4 h + r % 4,
-  // m = 32 wm + i.  Staged as [m][n] OutT rows (pitch + 16 bytes), then stored
-  // as 16-byte pieces of whole rows.
-  constexpr int kRowB = kPsTile * (int)sizeof(OutT), kPitchB = kRowB + 16;
-  static_assert(kPsTile * kPitchB <= STAGES * kPsStageBytes, "output staging fits the stages");
+  // m = TM / 2 wm + 32 mi + i.  Staged as [m][n] OutT rows (pitch + 16 bytes),
+  // then stored as 16-byte pieces of whole rows.
+  constexpr int kRowB = kPsTileN * (int)sizeof(OutT), kPitchB = kRowB + 16;
+  static_assert(TM * kPitchB <= STAGES * kStage, "output staging fits the stages");
   __syncthreads();  // every wave is done with the stages
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int nl = 32 * wn + 8 * q + 4 * h;
-    LDS_AS char* dst = smem + (32 * wm + i) * kPitchB + nl * (int)sizeof(OutT);
-    if constexpr (sizeof(OutT) == 4) {
-      *(LDS_AS floatx4*)dst = floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-    } else {
-      *(LDS_AS bf16x4*)dst = bf16x4{(__bf16)acc[4 * q], (__bf16)acc[4 * q + 1], (__bf16)acc[4 * q + 2],
-                                    (__bf16)acc[4 * q + 3]};
+  for (int mi = 0; mi < kMt; ++mi)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int nl = 32 * wn + 8 * q + 4 * h;
+      LDS_AS char* dst = smem + ((TM / 2) * wm + 32 * mi + i) * kPitchB + nl * (int)sizeof(OutT);
+      const floatx16& a = acc[mi];
+      if constexpr (sizeof(OutT) == 4) {
+        *(LDS_AS floatx4*)dst = floatx4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+      } else {
+        *(LDS_AS bf16x4*)dst =
+            bf16x4{(__bf16)a[4 * q], (__bf16)a[4 * q + 1], (__bf16)a[4 * q + 2], (__bf16)a[4 * q + 3]};
+      }
     }
-  }
   __syncthreads();
-  constexpr int kPieces = kPsTile * kRowB / 16, kPerRow = kRowB / 16;
+  constexpr int kPieces = TM * kRowB / 16, kPerRow = kRowB / 16;
 #pragma unroll
   for (int e = threadIdx.x; e < kPieces; e += 256) {
     const int ml = e / kPerRow, pc = e - ml * kPerRow;
@@ -1777,26 +1790,29 @@ hipError_t launch_verify(int32_t B, int32_t T, int32_t V, int32_t dtype, const v
   return hipGetLastError();
 }
 
-template <int S>
-hipError_t launch_staged(dim3 grid, hipStream_t stream, int M, int G, int K, int N, const void* x, const void* w,
-                         int32_t out_dtype, void* out, int tm, int tn, int64_t px, int64_t tl) {
-  const size_t lds = (size_t)S * kPsStageBytes;
+template <int S, int TM>
+hipError_t launch_staged(hipStream_t stream, int M, int G, int K, int N, const void* x, const void* w,
+                         int32_t out_dtype, void* out) {
+  const int tm = (M + TM - 1) / TM, tn = (N + kPsTileN - 1) / kPsTileN;
+  const int64_t tl = (int64_t)G * tm * tn, px = (tl + 7) / 8;
+  const dim3 grid((unsigned)(8 * px));
+  const size_t lds = (size_t)S * ps_stage_bytes<TM>();
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
-    const hipError_t e1 = hipFuncSetAttribute((const void*)mla_project_staged<float, S>,
+    const hipError_t e1 = hipFuncSetAttribute((const void*)mla_project_staged<float, S, TM>,
                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    const hipError_t e2 = hipFuncSetAttribute((const void*)mla_project_staged<__bf16, S>,
+    const hipError_t e2 = hipFuncSetAttribute((const void*)mla_project_staged<__bf16, S, TM>,
                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_err = e1 != hipSuccess ? e1 : e2;
   });
   if (attr_err != hipSuccess) return attr_err;
   if (out_dtype == kF32)
-    hipLaunchKernelGGL((mla_project_staged<float, S>), grid, dim3(256), lds, stream, M, G, K, N, (const __bf16*)x,
-                       (const __bf16*)w, (float*)out, tm, tn, (int)px, (int)tl);
+    hipLaunchKernelGGL((mla_project_staged<float, S, TM>), grid, dim3(256), lds, stream, M, G, K, N,
+                       (const __bf16*)x, (const __bf16*)w, (float*)out, tm, tn, (int)px, (int)tl);
   else
-    hipLaunchKernelGGL((mla_project_staged<__bf16, S>), grid, dim3(256), lds, stream, M, G, K, N, (const __bf16*)x,
-                       (const __bf16*)w, (__bf16*)out, tm, tn, (int)px, (int)tl);
+    hipLaunchKernelGGL((mla_project_staged<__bf16, S, TM>), grid, dim3(256), lds, stream, M, G, K, N,
+                       (const __bf16*)x, (const __bf16*)w, (__bf16*)out, tm, tn, (int)px, (int)tl);
   return hipGetLastError();
 }
 
@@ -1808,14 +1824,17 @@ hipError_t launch_project(int32_t M, int32_t G, int32_t K, int32_t N, const void
   const int64_t per_xcd = (tiles + 7) / 8;
   const dim3 grid((unsigned)(8 * per_xcd)), block(64 * kPjWaves);
   // staged form: k a multiple of 64, and every row offset within a tile's
-  // 64 rows fits the loads' 32-bit offsets
-  if (K % 64 == 0 && (int64_t)kPsTile * G * K * 2 < ((int64_t)1 << 31)) {
-    const int tm = (M + kPsTile - 1) / kPsTile, tn = (N + kPsTile - 1) / kPsTile;
-    const int64_t tl = (int64_t)G * tm * tn, px = (tl + 7) / 8;
-    const dim3 g2((unsigned)(8 * px));
-    // two stages hold all of k <= 128 (more resident workgroups); four otherwise
-    if (K <= 128) return launch_staged<2>(g2, stream, M, G, K, N, x, w, out_dtype, out, tm, tn, px, tl);
-    return launch_staged<4>(g2, stream, M, G, K, N, x, w, out_dtype, out, tm, tn, px, tl);
+  // 128 rows fits the loads' 32-bit offsets.  Two stages hold all of
+  // k <= 128 (more resident workgroups), four stream longer k.  With k <= 128
+  // and more than 64 rows, 128-row tiles read each weight row once per 128
+  // token rows (A/B on one box: 1024 rows x 64 heads, k 128 -> n 512, 6 %
+  // faster); with four stages their 96 KB of LDS leaves one workgroup per CU,
+  // and 64-row tiles are faster.
+  if (K % 64 == 0 && (int64_t)128 * G * K * 2 < ((int64_t)1 << 31)) {
+    if (K <= 128)
+      return M > 64 ? launch_staged<2, 128>(stream, M, G, K, N, x, w, out_dtype, out)
+                    : launch_staged<2, 64>(stream, M, G, K, N, x, w, out_dtype, out);
+    return launch_staged<4, 64>(stream, M, G, K, N, x, w, out_dtype, out);
   }
   const int nch = (K + kPjChunk - 1) / kPjChunk, per_wave = (nch + kPjWaves - 1) / kPjWaves;
 #define PJ_LAUNCH(T, GR) hipLaunchKernelGGL((mla_project_kernel<T, GR>), grid, block, 0, stream, M, G, K, N, (const __bf16*)x, \

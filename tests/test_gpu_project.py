@@ -64,9 +64,11 @@ CASES = [
     (70, 3, 520, 40),
     (32, 5, 40, 64),
     (64, 2, 1056, 136),
-    # the staged form (k a multiple of 64): tails in m and n, n below one tile
+    # the staged form (k a multiple of 64): tails in m and n, n below one tile;
+    # more than 64 rows with k <= 128 take 128-row tiles
     (3, 2, 192, 8),
     (130, 3, 640, 200),
+    (200, 2, 128, 72),
 ]
 
 
