@@ -1227,6 +1227,126 @@ mla_combine_balanced_kernel(int B, int M, int Dc, int NB, const int32_t* __restr
             po, pl, out_dtype, out, idx, lse);
 }
 
+// Balanced-plan merge, four rows per wavefront (M a multiple of 4 and Dc a
+// multiple of 8; the rows share their unit and so their slots).  A merge of
+// one row per wavefront spends its life waiting on three dependent loads
+// (tile prefix, slot lse, slot rows) with a few KB in flight; four rows per
+// wave put 4x the rows' loads in flight behind the same waits and quarter
+// the number of waves.  Each lane owns 8 consecutive columns of the four
+// rows; partial rows are read four slots at a time as raw bf16, a zero-weight
+// slot is dropped by a select (its row may hold anything).
+constexpr int kMergeRows = 4;
+
+__global__ void __launch_bounds__(256)
+mla_combine_balanced4_kernel(int B, int M, int Dc, int NB, const int32_t* __restrict__ prefix,
+                             const __bf16* __restrict__ po, const float* __restrict__ pl, int out_dtype,
+                             void* out, float* lse) {
+  const int lane = threadIdx.x & 63;
+  const int64_t idx0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kMergeRows;
+  if (idx0 >= (int64_t)B * M) return;
+  const int b = (int)(idx0 / M), r0 = (int)(idx0 - (int64_t)b * M);
+  const int groups = (M + kBalancedRows - 1) / kBalancedRows;
+  const int g = r0 / kBalancedRows, lr0 = r0 - g * kBalancedRows;
+  const int u = b * groups + g;
+  const int64_t W = prefix[B * groups];
+  const int64_t su = prefix[u], eu = prefix[u + 1];
+  if (su == eu) {  // no visible token: out = 0, lse = -inf
+    for (int rr = 0; rr < kMergeRows; ++rr) {
+      const int64_t ob = (idx0 + rr) * Dc;
+      for (int d = lane; d < Dc; d += 64) {
+        if (out_dtype == kBF16) ((__bf16*)out)[ob + d] = (__bf16)0.0f;
+        else ((float*)out)[ob + d] = 0.0f;
+      }
+      if (lse && lane == 0) lse[idx0 + rr] = neg_inf();
+    }
+    return;
+  }
+  const int64_t nb = W < NB ? W : NB;
+  const int k1 = (int)(((su + 1) * nb + W - 1) / W - 1);
+  const int k2 = (int)((eu * nb + W - 1) / W - 1);
+  if (k1 == k2) return;  // written by the split kernel
+  const int ns = k2 - k1 + 1;
+  auto slot_row = [&](int j) -> int64_t {  // row lr0 of partial j's slot
+    const int64_t slot = j == 0 ? 2LL * k1 + 1 : 2LL * (k1 + j);
+    return slot * kBalancedRows + lr0;
+  };
+  auto weight = [](float v, float mx) { return v == neg_inf() ? 0.0f : fast_exp2((v - mx) * kLog2e); };
+  // lane j holds the four rows' lse of partial j (the first 64; more are re-read)
+  float v0[kMergeRows], mx[kMergeRows], inv[kMergeRows], w0[kMergeRows], wsum[kMergeRows];
+#pragma unroll
+  for (int rr = 0; rr < kMergeRows; ++rr) v0[rr] = lane < ns ? pl[slot_row(lane) + rr] : neg_inf();
+#pragma unroll
+  for (int rr = 0; rr < kMergeRows; ++rr) {
+    float m = v0[rr];
+    for (int j = lane + 64; j < ns; j += 64) m = fmaxf(m, pl[slot_row(j) + rr]);
+    mx[rr] = wave_max(m);
+    w0[rr] = weight(v0[rr], mx[rr]);
+    float sm = w0[rr];
+    for (int j = lane + 64; j < ns; j += 64) sm += weight(pl[slot_row(j) + rr], mx[rr]);
+    wsum[rr] = wave_sum(sm);
+    inv[rr] = wsum[rr] > 0.0f ? 1.0f / wsum[rr] : 0.0f;
+  }
+  for (int d0 = 0; d0 < Dc; d0 += 512) {
+    const int d = d0 + 8 * lane;
+    const bool ok = d < Dc;
+    float acc[kMergeRows][8];
+#pragma unroll
+    for (int rr = 0; rr < kMergeRows; ++rr)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[rr][e] = 0.0f;
+    for (int j0 = 0; j0 < ns; j0 += 64) {
+      float wj[kMergeRows];
+#pragma unroll
+      for (int rr = 0; rr < kMergeRows; ++rr)
+        wj[rr] = (j0 == 0 ? w0[rr] : (j0 + lane < ns ? weight(pl[slot_row(j0 + lane) + rr], mx[rr]) : 0.0f)) *
+                 inv[rr];
+      const int cnt = ns - j0 < 64 ? ns - j0 : 64;
+      for (int jj = 0; jj < cnt; jj += 4) {
+        bf16x8 raw[4][kMergeRows];
+        float w[4][kMergeRows];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = jj + q < cnt ? jj + q : cnt - 1;  // past the end: re-read the last, weight 0
+          const __bf16* row = po + slot_row(j0 + j) * Dc + d;
+#pragma unroll
+          for (int rr = 0; rr < kMergeRows; ++rr) {
+            w[q][rr] = jj + q < cnt ? __shfl(wj[rr], j, 64) : 0.0f;
+            raw[q][rr] = ok ? *(const bf16x8*)(row + (int64_t)rr * Dc) : bf16x8{};
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int rr = 0; rr < kMergeRows; ++rr) {
+            const bool live = w[q][rr] != 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              acc[rr][e] = live ? __builtin_fmaf(w[q][rr], (float)raw[q][rr][e], acc[rr][e]) : acc[rr][e];
+          }
+      }
+    }
+    if (ok) {
+#pragma unroll
+      for (int rr = 0; rr < kMergeRows; ++rr) {
+        const int64_t ob = (idx0 + rr) * Dc + d;
+        if (out_dtype == kBF16) {
+          bf16x8 o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = (__bf16)acc[rr][e];
+          *(bf16x8*)((__bf16*)out + ob) = o;
+        } else {
+          *(floatx4*)((float*)out + ob) = floatx4{acc[rr][0], acc[rr][1], acc[rr][2], acc[rr][3]};
+          *(floatx4*)((float*)out + ob + 4) = floatx4{acc[rr][4], acc[rr][5], acc[rr][6], acc[rr][7]};
+        }
+      }
+    }
+  }
+  if (lse && lane == 0) {
+#pragma unroll
+    for (int rr = 0; rr < kMergeRows; ++rr) lse[idx0 + rr] = wsum[rr] > 0.0f ? mx[rr] + __logf(wsum[rr]) : neg_inf();
+  }
+}
+
 // ------------------------------------------------------------- KV append
 // Paged KV append with packing: token t of request b is stored at logical
 // position pos[b] + t, i.e. page page_table[b][pos / P], slot pos mod P
@@ -1766,6 +1886,12 @@ hipError_t launch_combine_balanced(int32_t B, int32_t M, int32_t Dc, int32_t NB,
                                    hipStream_t stream) {
   const int64_t n = (int64_t)B * M;
   if (n == 0) return hipSuccess;
+  if (M % kMergeRows == 0 && Dc % 8 == 0) {
+    const int64_t waves = n / kMergeRows;
+    hipLaunchKernelGGL(mla_combine_balanced4_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, B, M,
+                       Dc, NB, tile_prefix, (const __bf16*)part_o, part_lse, out_dtype, out, lse);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(mla_combine_balanced_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream,
                      B, M, Dc, NB, tile_prefix, (const __bf16*)part_o, part_lse, out_dtype, out, lse);
   return hipGetLastError();

@@ -127,6 +127,10 @@ BALANCED_CASES = {
     # two row groups per request (64 heads x 4 drafts), causal chain
     "causal_two_groups": small(3, batch=2, seq_lens=("fixed", (4, 3000)), decoys=2, index=43),
     "fp8": small(4, batch=3, seq_lens=("fixed", (100, 7000, 64)), decoys=2, index=44),
+    # rows per request not a multiple of 4 (the merge then takes one row per
+    # wavefront), and 132 rows: a second row group of four rows
+    "six_heads": small(1, batch=3, heads=6, seq_lens=("fixed", (3000, 17, 900)), decoys=2, index=45),
+    "heads_132": small(1, batch=2, heads=132, seq_lens=("fixed", (2500, 700)), decoys=2, index=46),
 }
 
 
