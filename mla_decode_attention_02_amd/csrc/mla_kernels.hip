@@ -1271,6 +1271,68 @@ mla_combine_balanced4_kernel(int B, int M, int Dc, int NB, const int32_t* __rest
     return slot * kBalancedRows + lr0;
   };
   auto weight = [](float v, float mx) { return v == neg_inf() ? 0.0f : fast_exp2((v - mx) * kLog2e); };
+  // Few partials (a unit spread over at most kFewSlots workgroups) and
+  // Dc <= 512: the partials' lse and all their rows are requested together
+  // right after the tile prefix, so the wave waits on one dependent round of
+  // loads instead of one for the lse and one per four partials; partials past
+  // ns are not read.  Same arithmetic, in the same order, as the general path.
+  constexpr int kFewSlots = 8;
+  if (ns <= kFewSlots && Dc <= 512) {
+    const int d = 8 * lane;
+    const bool ok = d < Dc;
+    float v[kMergeRows];
+#pragma unroll
+    for (int rr = 0; rr < kMergeRows; ++rr) v[rr] = lane < ns ? pl[slot_row(lane) + rr] : neg_inf();
+    bf16x8 raw[kFewSlots][kMergeRows];
+#pragma unroll
+    for (int j = 0; j < kFewSlots; ++j) {
+      const __bf16* row = po + slot_row(j < ns ? j : 0) * Dc + d;
+#pragma unroll
+      for (int rr = 0; rr < kMergeRows; ++rr)
+        raw[j][rr] = ok && j < ns ? *(const bf16x8*)(row + (int64_t)rr * Dc) : bf16x8{};
+    }
+    float m[kMergeRows], ws[kMergeRows], wl[kMergeRows], acc[kMergeRows][8];
+#pragma unroll
+    for (int rr = 0; rr < kMergeRows; ++rr) {
+      m[rr] = wave_max(v[rr]);
+      const float w = weight(v[rr], m[rr]);
+      ws[rr] = wave_sum(w);
+      wl[rr] = w * (ws[rr] > 0.0f ? 1.0f / ws[rr] : 0.0f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[rr][e] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kFewSlots; ++j) {
+      if (j >= ns) break;
+#pragma unroll
+      for (int rr = 0; rr < kMergeRows; ++rr) {
+        const float w = __shfl(wl[rr], j, 64);
+        const bool live = w != 0.0f;  // a zero-weight partial's row may hold anything
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[rr][e] = live ? __builtin_fmaf(w, (float)raw[j][rr][e], acc[rr][e]) : acc[rr][e];
+      }
+    }
+    if (ok) {
+#pragma unroll
+      for (int rr = 0; rr < kMergeRows; ++rr) {
+        const int64_t ob = (idx0 + rr) * Dc + d;
+        if (out_dtype == kBF16) {
+          bf16x8 o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = (__bf16)acc[rr][e];
+          *(bf16x8*)((__bf16*)out + ob) = o;
+        } else {
+          *(floatx4*)((float*)out + ob) = floatx4{acc[rr][0], acc[rr][1], acc[rr][2], acc[rr][3]};
+          *(floatx4*)((float*)out + ob + 4) = floatx4{acc[rr][4], acc[rr][5], acc[rr][6], acc[rr][7]};
+        }
+      }
+    }
+    if (lse && lane == 0) {
+#pragma unroll
+      for (int rr = 0; rr < kMergeRows; ++rr) lse[idx0 + rr] = ws[rr] > 0.0f ? m[rr] + __logf(ws[rr]) : neg_inf();
+    }
+    return;
+  }
   // lane j holds the four rows' lse of partial j (the first 64; more are re-read)
   float v0[kMergeRows], mx[kMergeRows], inv[kMergeRows], w0[kMergeRows], wsum[kMergeRows];
 #pragma unroll
