@@ -439,7 +439,11 @@ mla_split_mfma(SplitParams p, int groups) {
       if (tid == 0) p.tile_prefix[U] = W;
     }
     const int64_t nb = W < p.NB ? W : p.NB;  // no workgroup with an empty range
-    wk = blockIdx.x;
+    // Ranges are dealt so that each XCD (hardware block id mod 8; the grid
+    // is NB workgroups) runs a contiguous run of NB / 8 of them: the few
+    // workgroups that share a unit, and so read its query rows, then mostly
+    // share one L2.
+    wk = (p.NB & 7) == 0 ? (int)(blockIdx.x & 7) * (p.NB >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
     if (wk >= nb) return;
     // (W < 2^30, so the bounds fit in int32; read back as wave-uniform values)
     wx = __builtin_amdgcn_readfirstlane((int)(wk * (int64_t)W / nb));
