@@ -582,6 +582,10 @@ def main():
     roof["path_roofline_ms"] = round(max(t_hbm, t_mfma) * 1e3, 5)
     roof["path_frac"] = round(max(t_hbm, t_mfma) * 1e3 / ms_per_step, 4)
 
+    probe = hbm_read_probe() if bound == "hbm" else None
+    if probe is not None:
+        roof["frac_of_read_probe"] = round(achieved / probe["gbs"], 4)
+
     cpu = None if args.no_cpu else cpu_baseline(inp, args.cpu_budget)
     seq_desc = (f"U[{w.seq_lens[1]},{w.seq_lens[2]}]" if w.seq_lens[0] == "uniform"
                 else f"fixed {w.seq_lens[1][0]}") + f" seed {1000 + w.index}"
@@ -601,10 +605,35 @@ def main():
         "tokens_per_s": round(tokens_per_s, 1),
         "kv_gbs_unique": round(alg_path["kv_unique"] / (ms_per_step / 1e3) / 1e9, 2),
         "split_ms": round(split_avg, 5), "combine_ms": round(float(np.mean(comb_ms)), 5),
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": roof, "hbm_read_probe": probe, "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
+
+
+def hbm_read_probe(gib=4, reps=10):
+    """What a plain streaming read reaches on this GPU, as context for the
+    HBM roofline fraction (which stays against the 8 TB/s spec peak): the
+    library's streaming-read hook over `gib` GiB, 8 workgroups per compute
+    unit, median over `reps` runs timed with events on the current stream."""
+    import mla_decode_attention_02_amd as mla
+    x = torch.empty((gib << 30) // 4, dtype=torch.int32, device="cuda")
+    x.fill_(1)
+    sink = torch.empty(8 * mla.balanced_workgroups(), dtype=torch.int32, device="cuda")
+    mla.stream_read(x, sink)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        mla.stream_read(x, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del x, sink
+    ms = float(np.median(times))
+    return {"gbs": round((gib << 30) / (ms / 1e3) / 1e9, 1), "ms": round(ms, 4),
+            "how": f"mla_stream_read over {gib} GiB, {reps} runs, median"}
 
 
 if __name__ == "__main__":

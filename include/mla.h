@@ -321,6 +321,21 @@ int mla_gather_rows(const mla_problem* problem, const void* kv_pages, const int3
                     hipStream_t stream);
 
 /*
+ * Measurement hook: a plain streaming read, the reference point for the
+ * decode kernels' HBM rates (read bandwidth a simple kernel reaches on this
+ * device).  Reads the `bytes` bytes of src (device memory, 16-byte aligned,
+ * bytes a multiple of 16) once, in sink_len workgroups, and writes to sink[k]
+ * (device array of sink_len uint32) the XOR of the 32-bit words workgroup k
+ * read; the XOR over all of sink is the XOR of every 32-bit word of src.
+ * sink_len must lie in [1, 65536]; src may be NULL when bytes is 0 (sink is
+ * then all zeros); bad pointers, alignment or sizes give
+ * MLA_ERR_INVALID_ARG, a launch failure MLA_ERR_HIP.  Caller owns both
+ * buffers; nothing is allocated.
+ */
+int mla_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t sink_len,
+                    hipStream_t stream);
+
+/*
  * Host-side table check (the one checked mode runs): page_table_host [B, MP]
  * and seq_lens_host [B] are HOST arrays.  Returns MLA_OK, MLA_ERR_CHECK or
  * MLA_ERR_INVALID_ARG.

@@ -25,7 +25,7 @@ EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_decode_spl
            "mla_combine", "mla_balanced_workgroups",
            "mla_decode_split_balanced", "mla_combine_balanced", "mla_cascade_workspace_size",
            "mla_decode_cascade", "mla_append_kv", "mla_verify_greedy",
-           "mla_project", "mla_gather_rows",
+           "mla_project", "mla_gather_rows", "mla_stream_read",
            "mla_check_tables", "mla_status_string")
 
 BALANCED_ROWS = 128  # rows per unit of the balanced work list
@@ -74,6 +74,7 @@ def library():
     lib.mla_verify_greedy.argtypes = [i32, i32, i32, P, i32, P, P, P, P, P]
     lib.mla_project.argtypes = [i32, i32, i32, i32, P, P, i32, P, P]
     lib.mla_gather_rows.argtypes = [PP, P, P, i32, P, P, P, P]
+    lib.mla_stream_read.argtypes = [P, sz, P, i32, P]
     lib.mla_check_tables.argtypes = [PP, P, P]
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -400,6 +401,19 @@ def gather_rows(kv_pages, page_table, req, tok, *, d_latent, d_rope=None):
                                      req.numel(), _ptr(req), _ptr(tok), _ptr(out), _stream()),
            "mla_gather_rows")
     return out
+
+
+def stream_read(src, sink):
+    """Measurement hook: read the bytes of the contiguous device tensor `src`
+    once; sink (int32 device tensor, one entry per workgroup) receives the
+    XOR of the 32-bit words each workgroup read."""
+    dev = src.device
+    _require(src, "src", dev)
+    _require(sink, "sink", dev, dtype=torch.int32, ndim=1)
+    nbytes = src.numel() * src.element_size()
+    _check(library().mla_stream_read(_ptr(src), nbytes, _ptr(sink), sink.numel(), _stream()),
+           "mla_stream_read")
+    return sink
 
 
 def check_tables(problem, page_table_host, seq_lens_host):

@@ -507,6 +507,15 @@ int mla_gather_rows(const mla_problem* problem, const void* kv_pages, const int3
              : MLA_ERR_HIP;
 }
 
+int mla_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t sink_len,
+                    hipStream_t stream) {
+  if ((!src && bytes) || !sink || sink_len < 1 || sink_len > 65536) return MLA_ERR_INVALID_ARG;
+  if (bytes % 16 != 0 || (uintptr_t)src % 16 != 0 || (uintptr_t)sink % 4 != 0) return MLA_ERR_INVALID_ARG;
+  return mla::launch_stream_read(src, (int64_t)(bytes / 16), sink, sink_len, stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
 const char* mla_status_string(int status) {
   switch (status) {
     case MLA_OK: return "ok";

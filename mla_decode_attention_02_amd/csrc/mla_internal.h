@@ -85,5 +85,7 @@ hipError_t launch_project(int32_t M, int32_t G, int32_t K, int32_t N, const void
 hipError_t launch_gather(int32_t Dc, int32_t Dr, int32_t P, int32_t MP, int32_t kv_dtype,
                          const void* kv, const int32_t* page_table, int32_t n,
                          const int32_t* req, const int32_t* tok, void* out, hipStream_t stream);
+hipError_t launch_stream_read(const void* src, int64_t n16, unsigned* sink, int32_t blocks,
+                              hipStream_t stream);
 
 }  // namespace mla

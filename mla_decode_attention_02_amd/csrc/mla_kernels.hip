@@ -2053,4 +2053,39 @@ hipError_t launch_gather(int32_t Dc, int32_t Dr, int32_t P, int32_t MP, int32_t 
   return hipGetLastError();
 }
 
+// ------------------------------------------------------ streaming read probe
+// Measurement hook: reads n16 16-byte words once (grid-stride, eight loads in
+// flight per thread) and writes the XOR of everything each workgroup read to
+// sink[workgroup], which keeps every load live and makes the result checkable.
+__global__ void __launch_bounds__(256)
+mla_stream_read_kernel(const uintx4* __restrict__ src, int64_t n16, unsigned* __restrict__ sink) {
+  __shared__ unsigned part[4];
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  unsigned acc = 0;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    uintx4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n16; i += stride) {
+    const uintx4 v = src[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc ^= (unsigned)__shfl_xor((int)acc, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
+hipError_t launch_stream_read(const void* src, int64_t n16, unsigned* sink, int32_t blocks,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(mla_stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const uintx4*)src, n16, sink);
+  return hipGetLastError();
+}
+
 }  // namespace mla

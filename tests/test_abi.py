@@ -167,3 +167,18 @@ def test_project_argument_checks(mla):
         ptrs = [fake, fake, fake]
         ptrs[i] = ctypes.c_void_p(0x1008)            # 8-byte aligned only
         assert lib.mla_project(*ok, ptrs[0], ptrs[1], mla.MLA_DTYPE_BF16, ptrs[2], None) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_stream_read_argument_checks(mla):
+    """The streaming-read hook rejects null pointers, misalignment, ragged sizes
+    and sink lengths outside [1, 65536] on the host (the addresses below are
+    never dereferenced: every call fails validation first)."""
+    lib, E = mla.library(), mla.MLA_ERR_INVALID_ARG
+    a, s = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    assert lib.mla_stream_read(None, 1024, s, 8, None) == E
+    assert lib.mla_stream_read(a, 1024, None, 8, None) == E
+    assert lib.mla_stream_read(a, 1024, s, 0, None) == E
+    assert lib.mla_stream_read(a, 1024, s, 65537, None) == E
+    assert lib.mla_stream_read(a, 1000, s, 8, None) == E
+    assert lib.mla_stream_read(ctypes.c_void_p(4104), 1024, s, 8, None) == E
+    assert lib.mla_stream_read(a, 1024, ctypes.c_void_p(8194), 8, None) == E
