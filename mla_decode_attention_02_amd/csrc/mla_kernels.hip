@@ -616,17 +616,15 @@ mla_split_mfma(SplitParams p, int groups) {
     const float* sg;
     LDS_AS char* dst;
   };
-  // The kLoads direct-to-LDS loads of a later tile are spread over the
-  // whole step, the first kQkLoads between the score MFMAs (one every
-  // kQkEvery steps of the score loop) and the rest between the value MFMAs
-  // (one every kPvEvery), so that the CU's load issue never bursts.
+  // The kLoads direct-to-LDS loads of a later tile go out between the score
+  // MFMAs, one every kQkEvery steps of the score loop: early in the step, so
+  // that they have the most time to land, and spread, so that the CU's load
+  // issue never bursts.  (Issued between the value MFMAs too, as earlier
+  // versions did, they left the speculative-decode shape 2 % slower.)
   constexpr int kQkSteps = FP8 ? 18 : 36;
-  // (FP8 tiles are half the bytes and stay in the score loop)
-  constexpr int kQkLoads = FP8 ? kLoads : (kLoads * 36 + 67) / 68;
-  constexpr int kPvLoads = kLoads - kQkLoads;
+  constexpr int kQkLoads = kLoads;
   constexpr int kQkEvery = kQkSteps / kQkLoads;
-  constexpr int kPvEvery = kPvLoads > 0 ? 32 / kPvLoads : 33;
-  static_assert(kQkEvery * kQkLoads <= kQkSteps && kPvEvery * kPvLoads <= 32, "load spread");
+  static_assert(kQkEvery * kQkLoads <= kQkSteps, "load spread");
   auto scores = [&](LDS_AS char* st, floatx16& sacc, const Loader& ld, auto with_loads) {
     constexpr bool kLd = decltype(with_loads)::value;
     floatx16 s0;
@@ -764,11 +762,7 @@ mla_split_mfma(SplitParams p, int groups) {
   // of tile i after each MFMA (each step is its own scheduling region, so the
   // VALU work sits between the MFMAs instead of after them).
   auto values_softmax = [&](LDS_AS char* sv, const bf16x8 (&pw)[2], LDS_AS char* st, int i,
-                            floatx16& z, bf16x8 (&pb)[2], const Loader& ld, bool with_loads) {
-    auto pv_load = [&](int x2) {
-      if (kPvLoads > 0 && x2 % kPvEvery == kPvEvery - 1 && x2 / kPvEvery < kPvLoads && with_loads)
-        issue_piece<FP8, WAVES>(ld.tg, ld.sg, ld.dst, wave, lane, kQkLoads + x2 / kPvEvery);
-    };
+                            floatx16& z, bf16x8 (&pb)[2]) {
     const int lim_rel = lim - (cb + 32 * i);
     SoftmaxState sm{neg_inf(), neg_inf(), 0.0f, false};
     // FP8: the scales of this lane's 16 tokens (two runs of 8), read up front
@@ -816,7 +810,6 @@ mla_split_mfma(SplitParams p, int groups) {
         if (x2 + kAhead < 32) ring[x2 % kAhead] = vread(x2 + kAhead);
         acc[x2 & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pw[x2 >> 4], acc[x2 & 15], 0, 0, 0);
         softmax_step(x2, tscv, lim_rel, z, pb, sm, i);
-        pv_load(x2);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -839,7 +832,6 @@ mla_split_mfma(SplitParams p, int groups) {
         acc[x2 & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             e4m3x8_to_bf16((unsigned)v[0], (unsigned)v[1]), pw[x2 >> 4], acc[x2 & 15], 0, 0, 0);
         softmax_step(x2, tscv, lim_rel, z, pb, sm, i);
-        pv_load(x2);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -893,7 +885,7 @@ mla_split_mfma(SplitParams p, int groups) {
       }
       __builtin_amdgcn_sched_barrier(0);
       bf16x8 pcur[2];
-      values_softmax(stage_of(i + STAGES - 1), pprev, st, i, z, pcur, ld, i + kDepth < ntiles);
+      values_softmax(stage_of(i + STAGES - 1), pprev, st, i, z, pcur);
       pprev[0] = pcur[0];
       pprev[1] = pcur[1];
       // branch-free: past the last tile this re-reads a valid entry and is unused
