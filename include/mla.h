@@ -190,8 +190,12 @@ int mla_balanced_workgroups(int32_t* num_workgroups);
  * Split stage of the balanced work list on the MFMA kernels (Dc 512, Dr 64,
  * bf16 queries, bf16 or FP8 KV, P a multiple of 32, scale > 0; else
  * MLA_ERR_UNSUPPORTED, as when W could exceed 2^30).  Inputs as for
- * mla_decode().  Writes tile_prefix [U + 1] int32 (tile_prefix[u] = tiles of
- * the units before u, tile_prefix[U] = W) for the merge stage.  A segment
+ * mla_decode().  The units' 32-token tiles, each unit's preceded by a fixed
+ * start cost of 4 positions (a workgroup that starts a unit inside its range
+ * gets that many tiles fewer), are cut into num_workgroups equal ranges of
+ * positions.  Writes tile_prefix [U + 1] int32 (tile_prefix[u] = positions of
+ * the units before u, a unit without tiles counting 0; tile_prefix[U] = W)
+ * for the merge stage.  A segment
  * that is a whole unit writes its rows of out [B, T, H, Dc] (out_dtype) and
  * lse (if not NULL) directly.  Any other segment writes its normalised
  * partial, rounded to bf16, and its natural-log lse (fp32) to a slot: slot 2k

@@ -29,6 +29,7 @@ EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_decode_spl
            "mla_check_tables", "mla_status_string")
 
 BALANCED_ROWS = 128  # rows per unit of the balanced work list
+BALANCED_START_COST = 4  # positions the balanced work list charges for starting a unit
 
 
 class MLAError(RuntimeError):

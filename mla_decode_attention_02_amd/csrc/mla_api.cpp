@@ -91,8 +91,9 @@ size_t partial_bytes(const mla_problem* pr, int32_t S) {
 // must fit.
 bool balanced_size_ok(const mla_problem* pr) {
   const int64_t units = mla::balanced_units(pr->batch, pr->q_len, pr->num_heads);
-  const int64_t max_tiles = ((int64_t)pr->max_pages_per_seq * pr->page_size + 31) / 32;
-  return units < (int64_t)INT32_MAX / 2 && units * max_tiles < (int64_t)INT32_MAX / 2;
+  // positions per unit: its tiles plus the start cost
+  const int64_t max_pos = ((int64_t)pr->max_pages_per_seq * pr->page_size + 31) / 32 + mla::kUnitStartCost;
+  return units < (int64_t)INT32_MAX / 2 && units * max_pos < (int64_t)INT32_MAX / 2;
 }
 
 // Balanced work list (used by mla_decode when the library chooses the plan,

@@ -29,11 +29,14 @@ struct SplitParams {
   float* part_lse;             // [B, S, T*H] fp32 (!write_final)
   bool force_generic;          // run the VALU kernel even where the MFMA one applies
   // Balanced work list (MFMA kernels only; NB == 0 selects uniform chunks):
-  // the 32-token tiles of all units (request, group of kBalancedRows rows)
-  // are cut into NB equal contiguous ranges, one per workgroup.
+  // the 32-token tiles of all units (request, group of kBalancedRows rows),
+  // each unit with tiles preceded by kUnitStartCost positions that stand for
+  // the cost of starting a segment, are cut into NB equal contiguous ranges
+  // of positions, one per workgroup.
   int32_t NB;
-  int32_t* tile_prefix;        // [B * groups + 1] exclusive prefix of tiles per unit,
-                               // written by workgroup 0 for the merge
+  int32_t* tile_prefix;        // [B * groups + 1] exclusive prefix of positions per
+                               // unit (tiles + kUnitStartCost, 0 for a unit
+                               // without tiles), written by workgroup 0 for the merge
   // Cascade (uniform chunks only; Sp == 0 disables it): chunks 0..Sp-1 split
   // the first prefix_len tokens (a prefix every request shares) with the same
   // page-aligned bounds for all requests, chunks Sp..S-1 split [prefix_len, L_b).
@@ -43,6 +46,12 @@ struct SplitParams {
 
 // Rows per unit of the balanced work list (the MFMA kernels' workgroup rows).
 constexpr int32_t kBalancedRows = 128;
+
+// Positions the balanced work list charges for starting a unit, in tiles: a
+// workgroup whose range holds the start of a unit pays a second prologue
+// (query staging, pipeline fill) and epilogue, and so gets that many fewer
+// tiles.  4 measured best of 0, 2, 4, 6, 8 on the DeepSeek-shaped batch.
+constexpr int32_t kUnitStartCost = 4;
 
 // Number of units (request, row group) of the balanced work list.
 inline int64_t balanced_units(int32_t B, int32_t T, int32_t H) {

@@ -370,9 +370,11 @@ mla_split_mfma(SplitParams p, int groups) {
   //   are given ids 8 apart and share that XCD's L2 while they read the same
   //   pages.
   //   Balanced (p.NB > 0): the units' tiles, laid end to end (unit-major,
-  //   prefix sums in p.tile_prefix), are cut into NB equal contiguous ranges,
-  //   one per workgroup; a range crosses unit boundaries freely, so every
-  //   workgroup gets the same number of tiles whatever the length mix.
+  //   each unit's preceded by kUnitStartCost positions for the cost of
+  //   starting it; prefix sums in p.tile_prefix), are cut into NB equal
+  //   contiguous ranges, one per workgroup; a range crosses unit boundaries
+  //   freely, so every workgroup gets the same work whatever the length mix,
+  //   a workgroup that starts a unit inside its range that many tiles fewer.
   int ub = 0, ug = 0, us = 0;
   int wx = 0, wx1 = 0;
   int wu = 0, wk = 0, wsu = 0;  // balanced: current unit and its first tile
@@ -407,9 +409,9 @@ mla_split_mfma(SplitParams p, int groups) {
     const int per = (U + 64 * WAVES - 1) / (64 * WAVES);
     const int u0 = tid * per < U ? tid * per : U;
     const int u1 = u0 + per < U ? u0 + per : U;
-    auto unit_tiles = [&](int u) {
+    auto unit_tiles = [&](int u) {  // the unit's positions: tiles + start cost
       const int Lu = p.seq_lens[u / groups];
-      return Lu > 0 ? (Lu + 31) >> 5 : 0;
+      return Lu > 0 ? ((Lu + 31) >> 5) + kUnitStartCost : 0;
     };
     int run_sum = 0;
     for (int u = u0; u < u1; ++u) run_sum += unit_tiles(u);
@@ -438,7 +440,9 @@ mla_split_mfma(SplitParams p, int groups) {
       }
       if (tid == 0) p.tile_prefix[U] = W;
     }
-    const int64_t nb = W < p.NB ? W : p.NB;  // no workgroup with an empty range
+    // no workgroup with an empty range (a range may still hold only a unit's
+    // start positions: its workgroup then has no segment)
+    const int64_t nb = W < p.NB ? W : p.NB;
     // Ranges are dealt so that each XCD (hardware block id mod 8; the grid
     // is NB workgroups) runs a contiguous run of NB / 8 of them: the few
     // workgroups that share a unit, and so read its query rows, then mostly
@@ -494,26 +498,31 @@ mla_split_mfma(SplitParams p, int groups) {
     drow = final_out ? (int64_t)b * M + (int64_t)g * kRows
                      : ((int64_t)b * p.S + us) * M + (int64_t)g * kRows;
   } else {
+    // Unit wu occupies positions [su, eu): kUnitStartCost positions, then
+    // its tiles from ts = su + kUnitStartCost on.
     int su = wsu, eu;
-    for (;;) {  // skip units without tiles
+    for (;;) {  // skip units that end at or before wx (and units without tiles)
       b = wu / groups;
       L = uniform_load(p.seq_lens + b);
-      eu = su + (L > 0 ? (L + 31) >> 5 : 0);
+      eu = su + (L > 0 ? ((L + 31) >> 5) + kUnitStartCost : 0);
       if (eu > wx) break;
       ++wu;
       su = eu;
     }
+    const int ts = su + kUnitStartCost;
+    const int s0 = wx > ts ? (int)wx : ts;
     const int e = (int)(wx1 < eu ? wx1 : eu);
+    if (s0 >= e) break;  // the range ends inside the unit's start cost: none of its tiles here
     g = wu - b * groups;
-    cb = 32 * (int)(wx - su);
-    ce = 32 * (e - su);
+    cb = 32 * (s0 - ts);
+    ce = 32 * (e - ts);
     if (ce > L) ce = L;
     // Partial slots: [NB][2][kRows] rows.  Slot 0 holds the segment that
     // continues a unit begun in an earlier workgroup, slot 1 the one that
     // starts a unit and continues into later workgroups.
-    final_out = wx == su && e == eu;
+    final_out = s0 == ts && e == eu;
     drow = final_out ? (int64_t)b * M + (int64_t)g * kRows
-                     : ((int64_t)wk * 2 + (wx > su ? 0 : 1)) * kRows;
+                     : ((int64_t)wk * 2 + (s0 > ts ? 0 : 1)) * kRows;
     wx = e;
     ++wu;
     wsu = eu;
@@ -1182,11 +1191,12 @@ mla_combine_kernel(int B, int S, int rows, int Dc, const float* __restrict__ po,
 
 // ------------------------------------------------------- balanced merge
 // Merge for the balanced work list (same arithmetic as mla_combine_kernel).
-// With W tiles cut into nb = min(NB, W) ranges [k W / nb, (k+1) W / nb),
-// tile x lies in range ceil((x+1) nb / W) - 1.  A unit whose tiles [su, eu)
-// lie in ranges k1 < k2 has its partials in slot 1 of workgroup k1 and in
-// slot 0 of workgroups k1+1 .. k2 (slot rows [k][2][kBalancedRows]).  One
-// wave per output row.
+// With W positions cut into nb = min(NB, W) ranges [k W / nb, (k+1) W / nb),
+// position x lies in range ceil((x+1) nb / W) - 1.  A unit at positions
+// [su, eu) has its tiles at [su + kUnitStartCost, eu); when they lie in
+// ranges k1 < k2 its partials are in slot 1 of workgroup k1 and in slot 0 of
+// workgroups k1+1 .. k2 (slot rows [k][2][kBalancedRows]).  One wave per
+// output row.
 __global__ void __launch_bounds__(256)
 mla_combine_balanced_kernel(int B, int M, int Dc, int NB, const int32_t* __restrict__ prefix,
                             const __bf16* __restrict__ po, const float* __restrict__ pl,
@@ -1211,7 +1221,7 @@ mla_combine_balanced_kernel(int B, int M, int Dc, int NB, const int32_t* __restr
     return;
   }
   const int64_t nb = W < NB ? W : NB;
-  const int k1 = (int)(((su + 1) * nb + W - 1) / W - 1);
+  const int k1 = (int)(((su + kUnitStartCost + 1) * nb + W - 1) / W - 1);  // range of the first tile
   const int k2 = (int)((eu * nb + W - 1) / W - 1);
   if (k1 == k2) return;  // written by the split kernel
   const int ns = k2 - k1 + 1;
@@ -1258,7 +1268,7 @@ mla_combine_balanced4_kernel(int B, int M, int Dc, int NB, const int32_t* __rest
     return;
   }
   const int64_t nb = W < NB ? W : NB;
-  const int k1 = (int)(((su + 1) * nb + W - 1) / W - 1);
+  const int k1 = (int)(((su + kUnitStartCost + 1) * nb + W - 1) / W - 1);  // range of the first tile
   const int k2 = (int)((eu * nb + W - 1) / W - 1);
   if (k1 == k2) return;  // written by the split kernel
   const int ns = k2 - k1 + 1;

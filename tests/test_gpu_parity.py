@@ -151,8 +151,8 @@ def test_balanced_work_list(mla, monkeypatch, name, plan):
 @pytest.mark.parametrize("nw", [1, 3, 0])
 def test_balanced_stages(mla, nw):
     """The two balanced stages called directly, with few workgroups (each takes
-    many segments) and with the device's own count (0): the tile prefix is
-    exact, the output matches the oracle, and with the device's count it is
+    many segments) and with the device's own count (0): the position prefix
+    (tiles plus the start cost per unit) is exact, the output matches the oracle, and with the device's count it is
     bitwise the output of mla_decode."""
     w = BALANCED_CASES["mixed"]
     inp = synth.make_inputs(w)
@@ -174,7 +174,9 @@ def test_balanced_stages(mla, nw):
     torch.cuda.synchronize()
     L = inp["seq_lens"].astype(np.int64)
     tiles = np.repeat((np.maximum(L, 0) + 31) // 32, groups)
-    expect = np.concatenate([[0], np.cumsum(tiles)])
+    # positions per unit: its tiles plus the start cost, none for a unit without tiles
+    positions = np.where(tiles > 0, tiles + mla.BALANCED_START_COST, 0)
+    expect = np.concatenate([[0], np.cumsum(positions)])
     assert np.array_equal(prefix.cpu().numpy(), expect)
     o, l = out.double().cpu().numpy(), lse.double().cpu().numpy()
     ro, rl = oracle.attend(inp)
