@@ -189,6 +189,39 @@ def test_balanced_stages(mla, nw):
         assert np.array_equal(o, o2) and np.array_equal(l, l2)
 
 
+@pytest.mark.parametrize("lens,nw", [((320, 320), 3), ((320, 320, 40), 9), ((33, 320), 4), ((320, 320), 28)])
+def test_balanced_range_ends_in_start_cost(mla, lens, nw):
+    """Cuts where a workgroup's range ends inside a unit's start positions (it
+    then holds none of that unit's tiles; two 10-tile units in 3 ranges of
+    positions [0, 9), [9, 18), [18, 28) with a start cost of 4 put the end of
+    range 1 exactly at unit 1's first tile), and cuts where whole ranges hold
+    only start positions (their workgroups have no segment: ranges 0 and 4 of
+    9 over 10-, 10- and 2-tile units; 8 of 28 one-position ranges): every tile
+    still goes to exactly one workgroup and the output matches the oracle."""
+    w = small(1, batch=len(lens), seq_lens=("fixed", lens), decoys=2, index=47)
+    inp = synth.make_inputs(w)
+    dev = to_device(inp)
+    pr = mla.make_problem(dev["q_abs"], dev["q_rope"], dev["kv"], dev["page_table"],
+                          causal=w.causal, max_seq_len=w.max_seq_len)
+    groups = -(-w.rows // mla.BALANCED_ROWS)
+    prefix = torch.full((w.batch * groups + 1,), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((w.batch, w.q_len, w.heads, w.d_latent), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    lse = torch.empty((w.batch, w.q_len, w.heads), dtype=torch.float32, device="cuda")
+    slot_o = torch.full((2 * nw, mla.BALANCED_ROWS, w.d_latent), float("nan"), dtype=torch.bfloat16,
+                        device="cuda")
+    slot_l = torch.full((2 * nw, mla.BALANCED_ROWS), float("nan"), device="cuda")
+    mla.decode_split_balanced(pr, dev["q_abs"], dev["q_rope"], dev["kv"], dev["page_table"],
+                              dev["seq_lens"], float(inp["scale"]), nw, prefix, out, lse,
+                              slot_o, slot_l, kv_scales=dev["kv_scales"])
+    mla.combine_balanced(pr, nw, prefix, slot_o, slot_l, out, lse)
+    torch.cuda.synchronize()
+    o = out.double().cpu().numpy()
+    ro, _ = oracle.attend(inp)
+    assert np.isfinite(o).all()
+    assert_close(o, ro, tolerance(w), f"lens={lens} nw={nw}")
+
+
 # ------------------------------------------------------------ cascade decode
 
 @pytest.mark.parametrize("case", ["agentic", "short_requests", "fp8", "causal"])
