@@ -92,7 +92,7 @@ def cpu_baseline(inp, budget_s):
     return {
         "value": round(sub["kv_logical"] / dt / 1e9, 4), "unit": "GB/s",
         "tokens_per_s": round(len(pick) * w.q_len / dt, 3),
-        "cores": threads, "kind": "oracle",
+        "cores": threads, "kind": "oracle", **host_info(),
         "sample": f"{len(pick)} of {w.batch} requests ({int(L[pick].sum())} KV tokens, all "
                   f"{w.heads} heads x {w.q_len} query tokens), fp64 C oracle, {dt:.1f} s",
     }
@@ -108,7 +108,7 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def pmc_summary(pmc_dir, workload, calib_mib, out_path):
+def pmc_summary(pmc_dir, workload, num_splits, calib_mib, out_path=None):
     """Per-launch HBM traffic of the split kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
     counter reads for the calibration copy of calib_mib MiB in the same run."""
@@ -125,14 +125,21 @@ def pmc_summary(pmc_dir, workload, calib_mib, out_path):
 
     # the kernel-source hash the profiled runs printed in their JSON lines
     # (their logs sit beside the counter directory as <dir>_*.log)
-    seen = set()
+    seen, plans = set(), set()
     for logf in glob.glob(pmc_dir.rstrip("/") + "_*.log"):
         for ln in open(logf, errors="replace"):
             if ln.startswith("{") and "kernel_source_sha256_16" in ln:
-                seen.add(json.loads(ln)["kernel_source_sha256_16"])
-    if len(seen) > 1:
-        raise SystemExit(f"profiled runs disagree on the kernel source: {sorted(seen)}")
+                rec = json.loads(ln)
+                seen.add(rec["kernel_source_sha256_16"])
+                plans.add(rec["config"].get("plan_key"))
+    if len(seen) > 1 or len(plans) > 1:
+        raise SystemExit(f"profiled runs disagree: sources {sorted(seen)}, plans {sorted(map(str, plans))}")
     src_hash = seen.pop() if seen else kernel_source_hash()
+    plan_key = plans.pop() if plans else None
+    if out_path is None:
+        if plan_key is None:
+            raise SystemExit("no profiled run log names its plan; pass --pmc-out")
+        out_path = traffic_path(workload, plan_key)
 
     f_split, f_copy = per_kernel("FETCH_SIZE")
     w_split, w_copy = per_kernel("WRITE_SIZE")
@@ -142,8 +149,8 @@ def pmc_summary(pmc_dir, workload, calib_mib, out_path):
     fetch = float(np.mean(f_split)) * rf * 1024
     write = float(np.mean(w_split)) * wf * 1024
     rel = os.path.relpath(os.path.abspath(pmc_dir), ROOT)
-    run = (f"python -u $REPO/bench.py --steps 5 --warmup 2 --no-cpu --workload {workload} "
-           f"--calib-copy-mib {calib_mib}")
+    run = (f"python -u $REPO/bench.py --steps 5 --warmup 2 --no-cpu --no-sub --no-probe --workload {workload}"
+           f"{'' if num_splits < 0 else f' --num-splits {num_splits}'} --calib-copy-mib {calib_mib}")
     lines = [
         f"# HBM traffic of mla_split_mfma, workload {workload}",
         "",
@@ -152,10 +159,12 @@ def pmc_summary(pmc_dir, workload, calib_mib, out_path):
         "```",
         f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/{rel} -o pass3 -- {run}",
         f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/{rel} -o pass4 -- {run}",
-        f"python bench.py --pmc-summary {rel} --workload {workload} --calib-copy-mib {calib_mib}",
+        f"python bench.py --pmc-summary {rel} --workload {workload}"
+        f"{'' if num_splits < 0 else f' --num-splits {num_splits}'} --calib-copy-mib {calib_mib}",
         "```",
         "",
         f"kernel_source_sha256_16: {src_hash}",
+        f"plan: {plan_key}",
         f"dispatches: {len(f_split)} (FETCH_SIZE run), {len(w_split)} (WRITE_SIZE run)",
         f"FETCH_SIZE per dispatch (KiB, raw): {np.mean(f_split):.1f}",
         f"WRITE_SIZE per dispatch (KiB, raw): {np.mean(w_split):.1f}",
@@ -170,9 +179,17 @@ def pmc_summary(pmc_dir, workload, calib_mib, out_path):
     print("\n".join(lines))
 
 
-def recorded_traffic(workload):
-    """Traffic per launch recorded for this workload, if taken on the current kernel source."""
-    path = os.path.join(PROFILES, f"mla_split_mfma__{workload}__traffic.md")
+def traffic_path(workload, plan_key):
+    """Where the HBM-traffic summary of the split kernel for this workload and
+    launch configuration (plan key: "balanced", or "s<S>" for S uniform
+    chunks per request) lives under profiles/."""
+    return os.path.join(PROFILES, f"mla_split_mfma__{workload}__{plan_key}__traffic.md")
+
+
+def recorded_traffic(workload, plan_key):
+    """Traffic per launch recorded for this workload and launch configuration,
+    if taken on the current kernel source."""
+    path = traffic_path(workload, plan_key)
     if not os.path.exists(path):
         return None
     info = {}
@@ -396,141 +413,119 @@ def bench_project(mla, args):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="deepseek_v3_bf16",
-                    choices=[w.name for w in synth.WORKLOADS])
-    ap.add_argument("--num-splits", type=int, default=-1,
-                    help="override the split count (default: the workload's, else the library's)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run one plain device copy of this size (counter calibration)")
-    ap.add_argument("--pmc-summary", metavar="DIR",
-                    help="summarise FETCH_SIZE/WRITE_SIZE rocprofv3 CSVs in DIR and exit")
-    ap.add_argument("--pmc-out", metavar="FILE", help="where --pmc-summary writes its summary")
-    ap.add_argument("--cascade", action="store_true",
-                    help="decode with mla_decode_cascade over the workload's shared prefix")
-    ap.add_argument("--op", choices=("decode", "append", "verify", "project"), default="decode",
-                    help="decode (the default hot path), the paged KV append with FP8 packing, "
-                         "the greedy verification of speculative drafts, or the absorbed "
-                         "projections around one decode step of --workload")
-    args = ap.parse_args()
-    if args.pmc_summary:
-        pmc_summary(args.pmc_summary, args.workload, args.calib_copy_mib or 1024,
-                    args.pmc_out or os.path.join(PROFILES, f"mla_split_mfma__{args.workload}__traffic.md"))
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the decode on a single MI355X "
-              "(--gpus 1); multi-GPU runs are not part of it.", file=sys.stderr)
-        sys.exit(2)
-    import mla_decode_attention_02_amd as mla
-    mla.library()
-    torch.cuda.set_device(0)
-    if args.op == "append":
-        bench_append(mla, args)
-        return
-    if args.op == "project":
-        bench_project(mla, args)
-        return
-    if args.op == "verify":
-        bench_verify(mla, args)
-        return
+HEADLINE = "spec_decode_bf16"
+# The other graded workloads, measured in the same run and reported inside the
+# headline's JSON line: (workload, forced split count or None for the
+# library's own plan, label).
+SUB_RESULTS = (("deepseek_v3_bf16", None, "library plan"),
+               ("agentic_long_bf16", 16, "16 chunks per request, as configured"),
+               ("agentic_long_bf16", 0, "library plan"),
+               ("fp8_kv", None, "library plan"))
 
-    w = next(x for x in synth.WORKLOADS if x.name == args.workload)
-    inp = synth.make_inputs(w, poison=False)
+
+def host_info():
+    """Host cores and CPU model, recorded beside the oracle's time."""
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
+def measure_decode(mla, w, inp, args, S_req, cascade=False):
+    """Time `args.steps` decode steps of workload `w` on the device copies of
+    `inp`; returns the measurement record (no CPU baseline)."""
+    import ctypes
     kv_bytes = inp["kv"].nbytes + (0 if inp["kv_scales"] is None else inp["kv_scales"].nbytes)
     copies = max(2, min(8, math.ceil(4 * LLC_BYTES / kv_bytes)))
     sets = device_inputs(inp, copies)
     d0 = sets[0]
-    S_req = w.num_splits if args.num_splits < 0 else args.num_splits
     pr = mla.make_problem(d0["q_abs"], d0["q_rope"], d0["kv"], d0["page_table"],
                           causal=w.causal, num_splits=S_req, max_seq_len=w.max_seq_len)
     S = mla.num_splits(pr)
     B, T, H, Dc = d0["q_abs"].shape
     R = T * H
     out_dt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
-    part_o = torch.empty((B, S, R, Dc), dtype=torch.float32, device="cuda")
-    part_l = torch.empty((B, S, R), dtype=torch.float32, device="cuda")
     out = torch.empty((B, R, Dc), dtype=out_dt, device="cuda")
     lse = torch.empty((B, R), dtype=torch.float32, device="cuda")
     scale = float(inp["scale"])
 
     # Arguments are marshalled once per KV copy, so that the timed loop only
-    # makes the two C-ABI calls (the same two launches mla_decode makes) and
-    # records the HIP events around them on the launch stream.
-    import ctypes
+    # makes the C-ABI calls (the same launches mla_decode makes) and records
+    # the HIP events around them on the launch stream.
     lib = mla.library()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
     prs = mla.make_problem(d0["q_abs"], d0["q_rope"], d0["kv"], d0["page_table"],
                            causal=w.causal, num_splits=S, max_seq_len=w.max_seq_len)
-    split_args = [(ctypes.byref(prs), P(d["q_abs"]), P(d["q_rope"]), P(d["kv"]),
-                   P(d["kv_scales"]), P(d["page_table"]), P(d["seq_lens"]),
-                   ctypes.c_float(scale), S, P(part_o), P(part_l), stream) for d in sets]
-    comb_args = (B, S, R, Dc, P(part_o), P(part_l),
-                 mla.MLA_DTYPE_BF16 if out_dt == torch.bfloat16 else mla.MLA_DTYPE_F32,
-                 P(out), P(lse), stream)
-    ws = torch.empty(max(1, mla.workspace_size(prs)), dtype=torch.uint8, device="cuda")
-    dec_args = [(ctypes.byref(prs), P(d["q_abs"]), P(d["q_rope"]), P(d["kv"]),
-                 P(d["kv_scales"]), P(d["page_table"]), P(d["seq_lens"]), ctypes.c_float(scale),
-                 P(out), P(lse), P(ws), ws.numel(), stream) for d in sets]
-
     # mla_decode's own choice: the balanced work list when the library picks
     # the plan, the uniform plan would split, and the MFMA kernels serve the
     # shape (MLA_PLAN=uniform turns it off).  Its two stages are called one
     # by one so that the split kernel can be timed by itself.
     balanced = (S_req == 0 and S > 1 and w.d_latent == 512 and w.d_rope == 64
                 and w.q_dtype == "bf16" and w.kv_dtype in ("bf16", "fp8")
-                and not os.environ.get("MLA_PLAN", "").startswith("u"))
-    if balanced:
-        nw = mla.balanced_workgroups()
-        groups = -(-R // mla.BALANCED_ROWS)
-        prefix = torch.empty(B * groups + 1, dtype=torch.int32, device="cuda")
-        slot_o = torch.empty((2 * nw, mla.BALANCED_ROWS, Dc), dtype=torch.bfloat16, device="cuda")
-        slot_l = torch.empty((2 * nw, mla.BALANCED_ROWS), dtype=torch.float32, device="cuda")
-        bsplit_args = [(ctypes.byref(prs), P(d["q_abs"]), P(d["q_rope"]), P(d["kv"]),
-                        P(d["kv_scales"]), P(d["page_table"]), P(d["seq_lens"]),
-                        ctypes.c_float(scale), nw, P(prefix), P(out), P(lse), P(slot_o),
-                        P(slot_l), stream) for d in sets]
-        bcomb_args = (ctypes.byref(prs), nw, P(prefix), P(slot_o), P(slot_l), P(out), P(lse), stream)
-
-    if args.cascade:
+                and not os.environ.get("MLA_PLAN", "").startswith("u") and not cascade)
+    nw = 0
+    if cascade:
         if not w.shared_prefix:
             raise SystemExit("--cascade needs a workload with a shared prefix")
         need = ctypes.c_size_t(0)
         lib.mla_cascade_workspace_size(ctypes.byref(prs), w.shared_prefix, ctypes.byref(need))
         cws = torch.empty(max(1, need.value), dtype=torch.uint8, device="cuda")
-        casc_args = [(ctypes.byref(prs), P(d["q_abs"]), P(d["q_rope"]), P(d["kv"]), P(d["kv_scales"]),
-                      P(d["page_table"]), P(d["seq_lens"]), ctypes.c_float(scale), w.shared_prefix, P(out),
-                      P(lse), P(cws), cws.numel(), stream) for d in sets]
-        balanced = False
+        calls = [[(lib.mla_decode_cascade,
+                   (ctypes.byref(prs), P(d["q_abs"]), P(d["q_rope"]), P(d["kv"]), P(d["kv_scales"]),
+                    P(d["page_table"]), P(d["seq_lens"]), ctypes.c_float(scale), w.shared_prefix, P(out),
+                    P(lse), P(cws), cws.numel(), stream))] for d in sets]
+        plan = "cascade over the shared prefix (split and merge timed together)"
+    elif balanced:
+        nw = mla.balanced_workgroups()
+        groups = -(-R // mla.BALANCED_ROWS)
+        prefix = torch.empty(B * groups + 1, dtype=torch.int32, device="cuda")
+        slot_o = torch.empty((2 * nw, mla.BALANCED_ROWS, Dc), dtype=torch.bfloat16, device="cuda")
+        slot_l = torch.empty((2 * nw, mla.BALANCED_ROWS), dtype=torch.float32, device="cuda")
+        calls = [[(lib.mla_decode_split_balanced,
+                   (ctypes.byref(prs), P(d["q_abs"]), P(d["q_rope"]), P(d["kv"]), P(d["kv_scales"]),
+                    P(d["page_table"]), P(d["seq_lens"]), ctypes.c_float(scale), nw, P(prefix), P(out),
+                    P(lse), P(slot_o), P(slot_l), stream)),
+                  (lib.mla_combine_balanced,
+                   (ctypes.byref(prs), nw, P(prefix), P(slot_o), P(slot_l), P(out), P(lse), stream))]
+                 for d in sets]
+        plan = f"balanced work list, {nw} workgroups"
+    elif S == 1:
+        ws = torch.empty(max(1, mla.workspace_size(prs)), dtype=torch.uint8, device="cuda")
+        calls = [[(lib.mla_decode,
+                   (ctypes.byref(prs), P(d["q_abs"]), P(d["q_rope"]), P(d["kv"]), P(d["kv_scales"]),
+                    P(d["page_table"]), P(d["seq_lens"]), ctypes.c_float(scale), P(out), P(lse), P(ws),
+                    ws.numel(), stream))] for d in sets]
+        plan = "uniform, 1 chunk per request"
+    else:
+        part_o = torch.empty((B, S, R, Dc), dtype=torch.float32, device="cuda")
+        part_l = torch.empty((B, S, R), dtype=torch.float32, device="cuda")
+        calls = [[(lib.mla_decode_split,
+                   (ctypes.byref(prs), P(d["q_abs"]), P(d["q_rope"]), P(d["kv"]), P(d["kv_scales"]),
+                    P(d["page_table"]), P(d["seq_lens"]), ctypes.c_float(scale), S, P(part_o), P(part_l),
+                    stream)),
+                  (lib.mla_combine,
+                   (B, S, R, Dc, P(part_o), P(part_l),
+                    mla.MLA_DTYPE_BF16 if out_dt == torch.bfloat16 else mla.MLA_DTYPE_F32,
+                    P(out), P(lse), stream))] for d in sets]
+        plan = f"uniform, {S} chunks per request"
 
     def step(i, evs=None):
+        # evs[0] .. evs[1] bracket the split kernel (the first call), evs[1] ..
+        # evs[2] the merge (if any)
+        seq = calls[i % copies]
         if evs is not None:
             evs[0].record()
-        if args.cascade:
-            # split and merge in one call: the "split" events bracket both
-            rc = lib.mla_decode_cascade(*casc_args[i % copies])
-            if evs is not None:
-                evs[1].record()
-        elif balanced:
-            rc = lib.mla_decode_split_balanced(*bsplit_args[i % copies])
-            if evs is not None:
-                evs[1].record()
-            rc |= lib.mla_combine_balanced(*bcomb_args)
-        elif S == 1:
-            rc = lib.mla_decode(*dec_args[i % copies])
-            if evs is not None:
-                evs[1].record()
-        else:
-            rc = lib.mla_decode_split(*split_args[i % copies])
-            if evs is not None:
-                evs[1].record()
-            rc |= lib.mla_combine(*comb_args)
+        rc = seq[0][0](*seq[0][1])
+        if evs is not None:
+            evs[1].record()
+        for fn, a in seq[1:]:
+            rc |= fn(*a)
         if evs is not None:
             evs[2].record()
         if rc:
@@ -556,13 +551,14 @@ def main():
     split_ms = [e[0].elapsed_time(e[1]) for e in events]
     comb_ms = [e[1].elapsed_time(e[2]) for e in events]
     ms_per_step = wall * 1e3 / args.steps
+    del sets, calls
+    torch.cuda.empty_cache()
 
+    pkey = "balanced" if balanced else ("cascade" if cascade else f"s{S}")
     L = inp["seq_lens"]
-    alg_split = algorithmic(w, L, with_output=(S == 1))
+    alg_split = algorithmic(w, L, with_output=(S == 1 or balanced))
     alg_path = algorithmic(w, L, with_output=True)
     split_avg = float(np.mean(split_ms))
-    tokens_per_s = B * T / (ms_per_step / 1e3)
-    kv_gbs = alg_path["kv_logical"] / (ms_per_step / 1e3) / 1e9
     t_hbm = alg_path["bytes"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = alg_path["flops"] / (BF16_PEAK_TFLOPS * 1e12)
     bound = "hbm" if t_hbm >= t_mfma else "mfma"
@@ -574,38 +570,119 @@ def main():
         achieved = alg_split["flops"] / (split_avg / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
-    traffic = recorded_traffic(w.name)
-    roof["traffic"] = traffic
+    if cascade:
+        roof["traffic"] = None
+    else:
+        roof["traffic"] = recorded_traffic(w.name, pkey)
     roof["kernel"] = "mla_split_mfma" if w.d_latent == 512 else "mla_split_generic"
     roof["per_launch_algorithmic"] = alg_split["bytes"] if bound == "hbm" else alg_split["flops"]
     roof["kernel_avg_ms"] = round(split_avg, 5)
     roof["path_roofline_ms"] = round(max(t_hbm, t_mfma) * 1e3, 5)
     roof["path_frac"] = round(max(t_hbm, t_mfma) * 1e3 / ms_per_step, 4)
-
-    probe = hbm_read_probe() if bound == "hbm" else None
-    if probe is not None:
-        roof["frac_of_read_probe"] = round(achieved / probe["gbs"], 4)
-
-    cpu = None if args.no_cpu else cpu_baseline(inp, args.cpu_budget)
     seq_desc = (f"U[{w.seq_lens[1]},{w.seq_lens[2]}]" if w.seq_lens[0] == "uniform"
                 else f"fixed {w.seq_lens[1][0]}") + f" seed {1000 + w.index}"
+    return {
+        "workload": w.name, "plan": plan, "ms_per_step": round(ms_per_step, 5),
+        "kv_gbs": round(alg_path["kv_logical"] / (ms_per_step / 1e3) / 1e9, 2),
+        "kv_gbs_unique": round(alg_path["kv_unique"] / (ms_per_step / 1e3) / 1e9, 2),
+        "tokens_per_s": round(B * T / (ms_per_step / 1e3), 1),
+        "split_ms": round(split_avg, 5), "combine_ms": round(float(np.mean(comb_ms)), 5),
+        "roofline": roof,
+        "config": {"workload": w.name, "batch": B, "q_len": T, "heads": H, "d_latent": w.d_latent,
+                   "d_rope": w.d_rope, "page_size": w.page_size, "seq_lens": seq_desc,
+                   "kv_dtype": w.kv_dtype, "shared_prefix": w.shared_prefix, "causal": w.causal,
+                   "plan": plan, "plan_key": pkey, "kv_copies_rotated": copies,
+                   "parallelism": "single GPU"},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, choices=[w.name for w in synth.WORKLOADS])
+    ap.add_argument("--num-splits", type=int, default=-1,
+                    help="override the split count (default: the workload's, else the library's)")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="measure only --workload (no sub-results for the other workloads)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read probe")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--pmc-summary", metavar="DIR",
+                    help="summarise FETCH_SIZE/WRITE_SIZE rocprofv3 CSVs in DIR and exit")
+    ap.add_argument("--pmc-out", metavar="FILE", help="where --pmc-summary writes its summary")
+    ap.add_argument("--cascade", action="store_true",
+                    help="decode with mla_decode_cascade over the workload's shared prefix")
+    ap.add_argument("--op", choices=("decode", "append", "verify", "project"), default="decode",
+                    help="decode (the default hot path), the paged KV append with FP8 packing, "
+                         "the greedy verification of speculative drafts, or the absorbed "
+                         "projections around one decode step of --workload")
+    args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, args.workload, args.num_splits, args.calib_copy_mib or 1024,
+                    args.pmc_out)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the decode on a single MI355X "
+              "(--gpus 1); multi-GPU runs are not part of it.", file=sys.stderr)
+        sys.exit(2)
+    import mla_decode_attention_02_amd as mla
+    mla.library()
+    torch.cuda.set_device(0)
+    if args.op == "append":
+        bench_append(mla, args)
+        return
+    if args.op == "project":
+        bench_project(mla, args)
+        return
+    if args.op == "verify":
+        bench_verify(mla, args)
+        return
+
+    w = next(x for x in synth.WORKLOADS if x.name == args.workload)
+    inp = synth.make_inputs(w, poison=False)
+    S_req = w.num_splits if args.num_splits < 0 else args.num_splits
+    head = measure_decode(mla, w, inp, args, S_req, cascade=args.cascade)
+    print(f"# {w.name}: {head['plan']}: step {head['ms_per_step']} ms, split {head['split_ms']} ms, "
+          f"frac {head['roofline']['frac']}", file=sys.stderr, flush=True)
+    probe = None
+    if head["roofline"]["bound"] == "hbm" and not args.no_probe:
+        probe = hbm_read_probe()
+        head["roofline"]["frac_of_read_probe"] = round(head["roofline"]["achieved"] / probe["gbs"], 4)
+    cpu = None if args.no_cpu else cpu_baseline(inp, args.cpu_budget)
+    del inp
+
+    subs = []
+    if not args.no_sub and not args.cascade and args.workload == HEADLINE and args.num_splits < 0:
+        cache = {}
+        for name, S_sub, label in SUB_RESULTS:
+            ws = next(x for x in synth.WORKLOADS if x.name == name)
+            if name not in cache:
+                cache.clear()
+                cache[name] = synth.make_inputs(ws, poison=False)
+            rec = measure_decode(mla, ws, cache[name], args, ws.num_splits if S_sub is None else S_sub)
+            rec["label"] = label
+            print(f"# {name}: {rec['plan']}: step {rec['ms_per_step']} ms, split {rec['split_ms']} ms, "
+                  f"frac {rec['roofline']['frac']}", file=sys.stderr, flush=True)
+            subs.append(rec)
+        cache.clear()
+
     line = {
-        "metric": METRIC, "value": round(kv_gbs, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "metric": METRIC, "value": head["kv_gbs"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 KV, bf16 MFMA", "f32": "f32"}[w.kv_dtype],
         "data": "synthetic (seeded N(0,1)*sigma rows and queries, random page permutation)",
-        "config": {"workload": w.name, "batch": B, "q_len": T, "heads": H, "d_latent": w.d_latent,
-                   "d_rope": w.d_rope, "page_size": w.page_size, "seq_lens": seq_desc,
-                   "shared_prefix": w.shared_prefix, "causal": w.causal,
-                   "plan": ("cascade over the shared prefix (split and merge timed together)" if args.cascade
-                            else f"balanced work list, {nw} workgroups" if balanced
-                            else f"uniform, {S} chunks per request"),
-                   "kv_copies_rotated": copies, "parallelism": "single GPU"},
-        "tokens_per_s": round(tokens_per_s, 1),
-        "kv_gbs_unique": round(alg_path["kv_unique"] / (ms_per_step / 1e3) / 1e9, 2),
-        "split_ms": round(split_avg, 5), "combine_ms": round(float(np.mean(comb_ms)), 5),
-        "roofline": roof, "hbm_read_probe": probe, "cpu_baseline": cpu,
+        "config": head["config"],
+        "tokens_per_s": head["tokens_per_s"], "kv_gbs_unique": head["kv_gbs_unique"],
+        "split_ms": head["split_ms"], "combine_ms": head["combine_ms"],
+        "roofline": head["roofline"], "hbm_read_probe": probe, "cpu_baseline": cpu,
+        "sub_results": [{k: r[k] for k in ("workload", "label", "plan", "ms_per_step", "tokens_per_s",
+                                            "kv_gbs", "kv_gbs_unique", "split_ms", "combine_ms",
+                                            "roofline")} for r in subs],
         "kernel_source_sha256_16": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -173,6 +173,26 @@ def _validate(q_abs, q_rope, kv_pages, page_table, seq_lens, kv_scales):
             raise ValueError("kv_scales must be [num_pages, page_size]")
 
 
+def _outputs(pr, q_abs, out, lse):
+    """The caller's out [B,T,H,Dc] and lse [B,T,H] after checks of device,
+    dtype, contiguity and size, or new tensors where they are None."""
+    dev = q_abs.device
+    B, T, H, Dc = q_abs.shape
+    if out is None:
+        out = torch.empty((B, T, H, Dc), dtype=_torch_dtype(pr.out_dtype), device=dev)
+    else:
+        _require(out, "out", dev, dtype=_torch_dtype(pr.out_dtype))
+        if out.numel() != B * T * H * Dc:
+            raise ValueError(f"out must hold [B, T, H, Dc] = {(B, T, H, Dc)} elements")
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    else:
+        _require(lse, "lse", dev, dtype=torch.float32)
+        if lse.numel() != B * T * H:
+            raise ValueError(f"lse must hold [B, T, H] = {(B, T, H)} elements")
+    return out, lse
+
+
 def decode(q_abs, q_rope, kv_pages, page_table, seq_lens, scale, *, kv_scales=None,
            causal=False, num_splits=0, max_seq_len=0, out=None, lse=None, workspace=None,
            out_dtype=None):
@@ -181,18 +201,12 @@ def decode(q_abs, q_rope, kv_pages, page_table, seq_lens, scale, *, kv_scales=No
     pr = make_problem(q_abs, q_rope, kv_pages, page_table, causal=causal,
                       num_splits=num_splits, max_seq_len=max_seq_len, out_dtype=out_dtype)
     dev = q_abs.device
-    B, T, H, Dc = q_abs.shape
-    if out is None:
-        out = torch.empty((B, T, H, Dc), dtype=_torch_dtype(pr.out_dtype), device=dev)
-    else:
-        _require(out, "out", dev, dtype=_torch_dtype(pr.out_dtype))
-    if lse is None:
-        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
-    else:
-        _require(lse, "lse", dev, dtype=torch.float32)
+    out, lse = _outputs(pr, q_abs, out, lse)
     need = workspace_size(pr)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace is not None:
+        _require(workspace, "workspace", dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().mla_decode(ctypes.byref(pr), _ptr(q_abs), _ptr(q_rope), _ptr(kv_pages),
                                 _ptr(kv_scales), _ptr(page_table), _ptr(seq_lens),
@@ -209,20 +223,19 @@ def decode_cascade(q_abs, q_rope, kv_pages, page_table, seq_lens, scale, prefix_
     pr = make_problem(q_abs, q_rope, kv_pages, page_table, causal=causal, max_seq_len=max_seq_len,
                       out_dtype=out_dtype)
     dev = q_abs.device
-    B, T, H, Dc = q_abs.shape
-    if out is None:
-        out = torch.empty((B, T, H, Dc), dtype=_torch_dtype(pr.out_dtype), device=dev)
-    if lse is None:
-        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    out, lse = _outputs(pr, q_abs, out, lse)
     need = ctypes.c_size_t(0)
     _check(library().mla_cascade_workspace_size(ctypes.byref(pr), int(prefix_len), ctypes.byref(need)),
            "mla_cascade_workspace_size")
     if workspace is None:
         workspace = torch.empty(max(1, need.value), dtype=torch.uint8, device=dev)
+    else:
+        _require(workspace, "workspace", dev)
     _check(library().mla_decode_cascade(ctypes.byref(pr), _ptr(q_abs), _ptr(q_rope), _ptr(kv_pages),
                                         _ptr(kv_scales), _ptr(page_table), _ptr(seq_lens),
                                         ctypes.c_float(float(scale)), int(prefix_len), _ptr(out), _ptr(lse),
-                                        _ptr(workspace), workspace.numel(), _stream()),
+                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        _stream()),
            "mla_decode_cascade")
     return out, lse
 
@@ -271,7 +284,8 @@ def decode_split_balanced(problem, q_abs, q_rope, kv_pages, page_table, seq_lens
     if tile_prefix.numel() < problem.batch * groups + 1:
         raise ValueError("tile_prefix too small")
     _require(out, "out", dev, dtype=_torch_dtype(problem.out_dtype))
-    _require(lse, "lse", dev, dtype=torch.float32)
+    if lse is not None:  # the C ABI takes NULL: no lse output
+        _require(lse, "lse", dev, dtype=torch.float32)
     _require(slot_o, "slot_o", dev, dtype=torch.bfloat16)
     _require(slot_lse, "slot_lse", dev, dtype=torch.float32)
     if (slot_o.numel() < 2 * nw * BALANCED_ROWS * problem.d_latent
@@ -287,10 +301,18 @@ def decode_split_balanced(problem, q_abs, q_rope, kv_pages, page_table, seq_lens
 def combine_balanced(problem, num_workgroups, tile_prefix, slot_o, slot_lse, out, lse):
     """Merge stage of the balanced work list into out/lse."""
     dev = out.device
-    for t, name in ((tile_prefix, "tile_prefix"), (slot_o, "slot_o"), (slot_lse, "slot_lse"),
-                    (lse, "lse")):
-        _require(t, name, dev)
+    _require(tile_prefix, "tile_prefix", dev, dtype=torch.int32)
+    _require(slot_o, "slot_o", dev, dtype=torch.bfloat16)
+    _require(slot_lse, "slot_lse", dev, dtype=torch.float32)
+    if lse is not None:  # the C ABI takes NULL: no lse output
+        _require(lse, "lse", dev, dtype=torch.float32)
     _require(out, "out", dev, dtype=_torch_dtype(problem.out_dtype))
+    nw = int(num_workgroups)
+    groups = -(-problem.q_len * problem.num_heads // BALANCED_ROWS)
+    if (tile_prefix.numel() < problem.batch * groups + 1
+            or slot_o.numel() < 2 * nw * BALANCED_ROWS * problem.d_latent
+            or slot_lse.numel() < 2 * nw * BALANCED_ROWS):
+        raise ValueError("tile_prefix or slot buffers too small")
     _check(library().mla_combine_balanced(ctypes.byref(problem), int(num_workgroups),
                                           _ptr(tile_prefix), _ptr(slot_o), _ptr(slot_lse),
                                           _ptr(out), _ptr(lse), _stream()),

@@ -21,7 +21,8 @@ import math
 
 import numpy as np
 
-from .formats import f32_to_bf16_bits, quantize_rows_e4m3, BF16_NAN_BITS, E4M3_NAN_CODE
+from .formats import (f32_to_bf16_bits, f32_to_bf16_bits_blocked, quantize_rows_e4m3, BF16_NAN_BITS,
+                      E4M3_NAN_CODE)
 
 
 @dataclass(frozen=True)
@@ -166,7 +167,7 @@ def make_inputs(w, seed=None, poison=True, seq_lens=None):
             kv[perm[n_unique:]] = 0
     elif w.kv_dtype == "bf16":
         kv = np.empty((NP, P, D), dtype=np.uint16)
-        kv[perm[:n_unique]] = f32_to_bf16_bits(vals)
+        kv[perm[:n_unique]] = f32_to_bf16_bits_blocked(vals)
         fill = BF16_NAN_BITS if poison else 0
         kv[perm[n_unique:]] = fill
         if poison:

@@ -404,18 +404,31 @@ def test_checked_mode_rejects_bad_page(mla, monkeypatch):
 
 # ----------------------------------------------------- full-size workloads
 
-@pytest.mark.parametrize("index", [1, 2, 3, 4])
-def test_full_size_workload_sampled(mla, index):
-    """Full BASELINE shapes in the launch configuration the benchmark times;
-    a sample of requests is checked against the oracle one by one."""
+# Each graded workload at its full size, in every launch configuration the
+# benchmark times: the library's own plan (the balanced work list where the
+# uniform plan would split, one chunk per request for the speculative batch)
+# and, for the agentic batch, the 16 chunks per request it is configured with.
+FULL_SIZE_CASES = [(1, None), (2, None), (2, 0), (3, None), (4, None)]
+
+
+@pytest.mark.parametrize("index,num_splits", FULL_SIZE_CASES)
+def test_full_size_workload_every_request(mla, index, num_splits):
+    """Full shapes, every request and every output element against the oracle
+    (which takes tens of seconds on the host cores for the largest batches)."""
     w = synth.workload(index)
+    S = w.num_splits if num_splits is None else num_splits
+    print(f"full size {w.name} S={S}: inputs", flush=True)
     inp = synth.make_inputs(w)
-    out, lse = run_decode(mla, inp, num_splits=w.num_splits)
+    out, lse = run_decode(mla, inp, num_splits=S)
     assert np.isfinite(out).all()
-    L = inp["seq_lens"]
-    pick = sorted({int(np.argmin(L)), int(np.argmax(L)), 0, w.batch - 1})
-    ro, rl = oracle.attend(inp, req_ids=pick)
-    stats = assert_close(out[pick], ro, tolerance(w), f"{w.name} sampled")
-    print(f"{w.name}: sampled requests {pick} max_abs {stats[0]:.3e} mean_rel {stats[1]:.3e}")
+    print(f"full size {w.name} S={S}: oracle over {w.batch} requests", flush=True)
+    ro, rl = oracle.attend(inp)
+    stats = assert_close(out, ro, tolerance(w), f"{w.name} S={S}")
+    # the bar must hold per request too, not only over the whole batch
+    worst = max(metrics(out[b], ro[b])[1] for b in range(w.batch))
+    print(f"{w.name} S={S}: all {w.batch} requests max_abs {stats[0]:.3e} mean_rel {stats[1]:.3e} "
+          f"(worst request mean_rel {worst:.3e})", flush=True)
+    assert worst <= tolerance(w)[1]
     fin = np.isfinite(rl)
-    assert np.abs(lse[pick][fin] - rl[fin]).max() <= 1e-3 * max(1.0, np.abs(rl).max())
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.abs(lse[fin] - rl[fin]).max() <= 1e-3 * max(1.0, np.abs(rl[fin]).max())
