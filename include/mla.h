@@ -28,9 +28,11 @@
  *
  * Conventions for every entry point:
  *   - All array arguments are DEVICE pointers unless marked "host"; the
- *     caller owns every buffer.  The library allocates no device memory,
- *     keeps no state between calls and never synchronises the stream (except
- *     in checked mode, see MLA_CHECK below).
+ *     caller owns every buffer.  The library allocates no device memory
+ *     (its one static device array, the scratch of mla_decode_no_alloc, comes
+ *     with the loaded code object), keeps no state between calls (that
+ *     array's contents aside) and never synchronises the stream (except in
+ *     checked mode, see MLA_CHECK below).
  *   - Work is enqueued on `stream` in order; results are ready when the
  *     stream reaches that point.  Calls on different streams may overlap.
  *   - Every function returns an mla_status code; no C++ exception crosses
@@ -73,7 +75,9 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = -2, /* well-formed, but no kernel for this combination */
   MLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than mla_workspace_size() */
   MLA_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
-  MLA_ERR_CHECK = -5        /* checked mode found a bad page id or seq_len */
+  MLA_ERR_CHECK = -5,       /* checked mode found a bad page id or seq_len */
+  MLA_ERR_SCRATCH = -6      /* mla_decode_no_alloc: the problem needs more workspace than
+                               MLA_STATIC_SCRATCH_BYTES */
 } mla_status;
 
 /* Shape and types of one decode call (host struct, passed by pointer). */
@@ -142,6 +146,34 @@ int mla_decode(const mla_problem* problem, const void* q_absorbed, const void* q
                const void* kv_pages, const float* kv_scales, const int32_t* page_table,
                const int32_t* seq_lens, float scale, void* out, float* lse, void* workspace,
                size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the library's static device scratch used by mla_decode_no_alloc
+ * (72 MiB: the balanced work list's slots for 256 compute units take 64 MiB). */
+#define MLA_STATIC_SCRATCH_BYTES ((size_t)72 << 20)
+
+/*
+ * mla_decode for callers that cannot allocate device memory: code recorded
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, plan, kernels and results as mla_decode()
+ * (bitwise), but the workspace is a static device array inside the library
+ * (MLA_STATIC_SCRATCH_BYTES, one copy per device, held until the process
+ * ends), so no workspace is passed; the caller still owns q, kv, tables and
+ * out/lse.  Nothing is allocated or freed by this call (the array's device
+ * address is looked up once per device on the first call there).  Returns
+ * MLA_ERR_SCRATCH, with nothing enqueued, when the workspace of the plan
+ * this call runs exceeds MLA_STATIC_SCRATCH_BYTES: the balanced work list's
+ * (64 MiB of bf16 slots and 256 KiB of slot lse for 256 compute units, plus
+ * 4 bytes of tile prefix per row group) fits up to about two million row
+ * groups; the uniform plan's while B * S * T * H * (d_latent + 1) * 4 bytes
+ * does.  Every call on a device shares that device's array and leaves its
+ * contents behind; nothing in it has to start at zero (every word a call
+ * reads there was written earlier in the same call).  Calls that overlap on
+ * one device (other streams, other host threads) race and must be serialised
+ * by the caller.
+ */
+int mla_decode_no_alloc(const mla_problem* problem, const void* q_absorbed, const void* q_rope,
+                        const void* kv_pages, const float* kv_scales, const int32_t* page_table,
+                        const int32_t* seq_lens, float scale, void* out, float* lse, hipStream_t stream);
 
 /*
  * Split stage only, with S = num_splits >= 1 chunks (problem->num_splits is

@@ -19,14 +19,15 @@ LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
 MLA_DTYPE_F32, MLA_DTYPE_BF16, MLA_DTYPE_FP8_E4M3 = 0, 1, 2
 MLA_OK = 0
 MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE = -1, -2, -3
-MLA_ERR_HIP, MLA_ERR_CHECK = -4, -5
+MLA_ERR_HIP, MLA_ERR_CHECK, MLA_ERR_SCRATCH = -4, -5, -6
+STATIC_SCRATCH_BYTES = 72 << 20  # MLA_STATIC_SCRATCH_BYTES
 
 EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_decode_split",
            "mla_combine", "mla_balanced_workgroups",
            "mla_decode_split_balanced", "mla_combine_balanced", "mla_cascade_workspace_size",
            "mla_decode_cascade", "mla_append_kv", "mla_verify_greedy",
            "mla_project", "mla_gather_rows", "mla_stream_read",
-           "mla_check_tables", "mla_status_string")
+           "mla_check_tables", "mla_decode_no_alloc", "mla_status_string")
 
 BALANCED_ROWS = 128  # rows per unit of the balanced work list
 BALANCED_START_COST = 4  # positions the balanced work list charges for starting a unit
@@ -77,6 +78,7 @@ def library():
     lib.mla_gather_rows.argtypes = [PP, P, P, i32, P, P, P, P]
     lib.mla_stream_read.argtypes = [P, sz, P, i32, P]
     lib.mla_check_tables.argtypes = [PP, P, P]
+    lib.mla_decode_no_alloc.argtypes = [PP, P, P, P, P, P, P, ctypes.c_float, P, P, P]
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     for name in EXPORTS[:-1]:
@@ -212,6 +214,22 @@ def decode(q_abs, q_rope, kv_pages, page_table, seq_lens, scale, *, kv_scales=No
                                 _ptr(kv_scales), _ptr(page_table), _ptr(seq_lens),
                                 ctypes.c_float(float(scale)), _ptr(out), _ptr(lse),
                                 _ptr(workspace), ws_bytes, _stream()), "mla_decode")
+    return out, lse
+
+
+def decode_no_alloc(q_abs, q_rope, kv_pages, page_table, seq_lens, scale, *, kv_scales=None,
+                    causal=False, num_splits=0, max_seq_len=0, out=None, lse=None, out_dtype=None):
+    """mla_decode with the library's static device scratch as its workspace
+    (``mla_decode_no_alloc``): no workspace is allocated for the call.
+    Returns (out, lse); out/lse are allocated here only when not given."""
+    _validate(q_abs, q_rope, kv_pages, page_table, seq_lens, kv_scales)
+    pr = make_problem(q_abs, q_rope, kv_pages, page_table, causal=causal,
+                      num_splits=num_splits, max_seq_len=max_seq_len, out_dtype=out_dtype)
+    out, lse = _outputs(pr, q_abs, out, lse)
+    _check(library().mla_decode_no_alloc(ctypes.byref(pr), _ptr(q_abs), _ptr(q_rope), _ptr(kv_pages),
+                                         _ptr(kv_scales), _ptr(page_table), _ptr(seq_lens),
+                                         ctypes.c_float(float(scale)), _ptr(out), _ptr(lse), _stream()),
+           "mla_decode_no_alloc")
     return out, lse
 
 

@@ -278,10 +278,16 @@ int mla_decode_split(const mla_problem* problem, const void* q_absorbed, const v
   return mla::launch_split(p, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-int mla_decode(const mla_problem* problem, const void* q_absorbed, const void* q_rope,
-               const void* kv_pages, const float* kv_scales, const int32_t* page_table,
-               const int32_t* seq_lens, float scale, void* out, float* lse, void* workspace,
-               size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// mla_decode with the workspace either the caller's (static_scratch false)
+// or the library's static device scratch (true: workspace arguments unused).
+int decode_impl(const mla_problem* problem, const void* q_absorbed, const void* q_rope,
+                const void* kv_pages, const float* kv_scales, const int32_t* page_table,
+                const int32_t* seq_lens, float scale, void* out, float* lse, void* workspace,
+                size_t workspace_bytes, bool static_scratch, hipStream_t stream) {
   int rc = validate_problem(problem);
   if (rc) return rc;
   rc = validate_inputs(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table, seq_lens);
@@ -290,14 +296,27 @@ int mla_decode(const mla_problem* problem, const void* q_absorbed, const void* q
   if (!out) return MLA_ERR_INVALID_ARG;
   const int32_t S = plan_splits(problem);
   const int32_t NB = balanced_shape(problem) && !env_force_uniform() ? device_cus() : 0;
-  const size_t need = decode_workspace(problem, S, NB);
-  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
-    return MLA_ERR_WORKSPACE;
-  rc = run_checked_mode(problem, page_table, seq_lens, stream);
-  if (rc) return rc;
   SplitParams p = make_params(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table,
                               seq_lens, scale, S);
-  if (NB > 0 && mla::pick_kernel(p) != mla::Kernel::kGeneric) {
+  const bool balanced = NB > 0 && mla::pick_kernel(p) != mla::Kernel::kGeneric;
+  if (static_scratch) {
+    // the workspace of the plan this call runs
+    static_assert(mla::kStaticScratchBytes == MLA_STATIC_SCRATCH_BYTES, "header and library agree");
+    const size_t need = balanced ? balanced_layout(problem, NB).total : (S > 1 ? partial_bytes(problem, S) : 0);
+    if (need > mla::kStaticScratchBytes) return MLA_ERR_SCRATCH;
+    workspace = nullptr;
+    workspace_bytes = mla::kStaticScratchBytes;
+    if (need > 0 && mla::static_scratch(&workspace) != hipSuccess) return MLA_ERR_HIP;
+  } else {
+    // the caller's workspace is sized by mla_workspace_size(): every plan this
+    // problem may take
+    const size_t need = decode_workspace(problem, S, NB);
+    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
+      return MLA_ERR_WORKSPACE;
+  }
+  rc = run_checked_mode(problem, page_table, seq_lens, stream);
+  if (rc) return rc;
+  if (balanced) {
     // the stages of mla_decode_split_balanced and mla_combine_balanced,
     // arguments already validated
     const BalancedLayout l = balanced_layout(problem, NB);
@@ -332,6 +351,25 @@ int mla_decode(const mla_problem* problem, const void* q_absorbed, const void* q
                              problem->out_dtype, out, lse, stream) == hipSuccess
              ? MLA_OK
              : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode(const mla_problem* problem, const void* q_absorbed, const void* q_rope,
+               const void* kv_pages, const float* kv_scales, const int32_t* page_table,
+               const int32_t* seq_lens, float scale, void* out, float* lse, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table, seq_lens, scale, out,
+                     lse, workspace, workspace_bytes, false, stream);
+}
+
+int mla_decode_no_alloc(const mla_problem* problem, const void* q_absorbed, const void* q_rope,
+                        const void* kv_pages, const float* kv_scales, const int32_t* page_table,
+                        const int32_t* seq_lens, float scale, void* out, float* lse, hipStream_t stream) {
+  return decode_impl(problem, q_absorbed, q_rope, kv_pages, kv_scales, page_table, seq_lens, scale, out,
+                     lse, nullptr, 0, true, stream);
 }
 
 int mla_balanced_workgroups(int32_t* num_workgroups) {
@@ -525,6 +563,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MLA_ERR_HIP: return "HIP runtime or launch failure";
     case MLA_ERR_CHECK: return "checked mode: page id or seq_len out of range";
+    case MLA_ERR_SCRATCH: return "problem needs more workspace than the static scratch of mla_decode_no_alloc holds";
     default: return "unknown status";
   }
 }

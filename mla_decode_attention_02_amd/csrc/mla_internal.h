@@ -97,4 +97,11 @@ hipError_t launch_gather(int32_t Dc, int32_t Dr, int32_t P, int32_t MP, int32_t 
 hipError_t launch_stream_read(const void* src, int64_t n16, unsigned* sink, int32_t blocks,
                               hipStream_t stream);
 
+// Size of the library's static device scratch (mla_decode_no_alloc).
+constexpr size_t kStaticScratchBytes = (size_t)72 << 20;
+
+// Device address of the static scratch on the current device (looked up once
+// per device, then cached).
+hipError_t static_scratch(void** ptr);
+
 }  // namespace mla

@@ -2090,4 +2090,34 @@ hipError_t launch_stream_read(const void* src, int64_t n16, unsigned* sink, int3
   return hipGetLastError();
 }
 
+// ------------------------------------------------------- static scratch
+// Device memory for mla_decode_no_alloc, the entry point for callers that
+// cannot allocate: the workspace of one decode (balanced work list slots and
+// tile prefix, or uniform-plan partials) lives in this file-scope array, one
+// copy per device, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current and kept in per_device below.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
+}
+
 }  // namespace mla

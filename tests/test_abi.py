@@ -182,3 +182,15 @@ def test_stream_read_argument_checks(mla):
     assert lib.mla_stream_read(a, 1000, s, 8, None) == E
     assert lib.mla_stream_read(ctypes.c_void_p(4104), 1024, s, 8, None) == E
     assert lib.mla_stream_read(a, 1024, ctypes.c_void_p(8194), 8, None) == E
+
+
+def test_no_alloc_rejects_oversized_workspace_before_any_launch(mla):
+    """mla_decode_no_alloc refuses, on the host, a problem whose workspace
+    (here the uniform plan's partials at 64 forced splits, ~1 GB) exceeds the
+    static scratch; the pointers are never dereferenced."""
+    pr = ds_problem(mla, num_splits=64)
+    dummy = ctypes.c_void_p(0x1000)
+    rc = mla.library().mla_decode_no_alloc(ctypes.byref(pr), dummy, dummy, dummy, None, dummy, dummy,
+                                           ctypes.c_float(0.1), dummy, None, None)
+    assert rc == mla.MLA_ERR_SCRATCH
+    assert "static scratch" in mla.status_string(rc)
