@@ -18,6 +18,7 @@
 //   mla_gather_kernel                  test hook for the page-table loader.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <mutex>
 #include <type_traits>
@@ -43,14 +44,23 @@ constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+template <typename T>
+__device__ __forceinline__ T uniform_load(const T* p) {
+  // wave-uniform address: read through the scalar cache
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // ------------------------------------------------------------------ loader
 // Physical row of logical token j of request b: the block table maps the
 // request's logical page j / P to a physical page, and j mod P is the slot in
-// it ("推理优化" tag page, PagedAttention article).  Every kernel resolves
-// rows through this one routine.
+// it ("推理优化" tag page, PagedAttention article).  The decode kernels and the
+// gather hook resolve rows through this routine; kUniform reads the table
+// entry through the scalar cache (b and j the same in every lane).
+template <bool kUniform = false>
 __device__ __forceinline__ int64_t kv_row_index(const int32_t* __restrict__ page_table, int MP,
                                                 int P, int b, int j) {
-  const int page = page_table[(int64_t)b * MP + j / P];
+  const int32_t* entry = page_table + (int64_t)b * MP + j / P;
+  const int page = kUniform ? uniform_load(entry) : *entry;
   return (int64_t)page * P + (j % P);
 }
 
@@ -297,12 +307,6 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
   }
 }
 
-template <typename T>
-__device__ __forceinline__ T uniform_load(const T* p) {
-  // wave-uniform address: read through the scalar cache
-  return *(const __attribute__((address_space(4))) T*)p;
-}
-
 // Score-tile MFMAs in inline assembly, with the accumulator constrained to
 // VGPRs.  The output accumulators take all 256 AGPRs; the compiler's builtin
 // would put this accumulator in AGPRs as well and shuffle output blocks out
@@ -322,6 +326,9 @@ __device__ __forceinline__ void mfma_v0(floatx16& c, const bf16x8& a, const bf16
 __device__ __forceinline__ void mfma_v(floatx16& c, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
+// mfma_drain() waits out the MFMA result latency before any other
+// instruction may read or write an accumulator the asm MFMAs above wrote.
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 __device__ __forceinline__ void mfma_v_last(floatx16& c, const bf16x8& a, const bf16x8& b) {
   asm volatile(
       "s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
@@ -985,6 +992,644 @@ mla_split_mfma(SplitParams p, int groups) {
     else if (p.lse) p.lse[orow] = lse_v;
   }
   }  // segments
+}
+
+// --------------------------------------------- MFMA split kernel, wave pairs
+// One workgroup = 8 wavefronts = the 128 query rows of one unit (request b,
+// row group g; row r = t * H + h, the query-token fold), as four pairs: pair
+// p (waves p and p + 4) owns rows 32p .. 32p + 31.  The pair splits both
+// contractions in halves: wave p (role 0) forms the partial scores over dims
+// [0, 288) of the 576-deep dot and owns output columns [0, 256); wave p + 4
+// (role 1) takes dims [288, 576) and columns [256, 512).  A wave so holds 72
+// query registers and 128 accumulators, and two waves share each SIMD: one
+// issues while the other waits.
+//
+// Scores are S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (a row's 32 token
+// scores sit in one lane pair), values O^T += V^T P^T with V read transposed
+// from the same LDS tile.  Per tile i (32 tokens), in two phases:
+//   phase 1  both waves score tile i (18 MFMAs, one chain) interleaved with
+//            their half of the value product of tile i - 1 (16 MFMAs); role 1
+//            writes its partial score tile to the pair's LDS slot;
+//   barrier
+//   phase 2  role 0 adds the partial, runs the softmax of tile i and writes
+//            the bf16 weights and the rescale factor to the slot; role 1
+//            refills the stage freed by tile i - 1 (bf16 KV: tile i + 2 by
+//            direct HBM -> LDS loads) or converts the next FP8 tile to bf16
+//            (E4M3 KV: raw tiles are loaded three ahead, each converted once
+//            for the whole workgroup);
+//   barrier.
+// LDS: bf16 KV -- three tile stages; E4M3 KV -- two bf16 stages of converted
+// tiles (plus their 32 token scales) and three raw E4M3 stages; and four 4 KB
+// exchange slots (role 1's partial scores, then role 0's weights, rescale
+// factors and, at the end, 1 / normaliser).
+constexpr int kPairWaves = 8;
+constexpr int kPairRows = 32 * 4;
+constexpr int kRawTileBytes = 32 * 576;          // E4M3 codes of one tile
+constexpr int kRawStage = kRawTileBytes + 1024;  // + the 32 scales, 8 copies
+constexpr int kXchgSlot = 4096;
+constexpr int kRowPitch = 1024 + 16;             // staged query / output rows
+constexpr int kQRegion = 32 * kRowPitch + 32 * 128;
+// Of a wave's 18 query fragments (16 dims each) the first kQReg stay in
+// registers and the last kQLds are re-read from LDS every tile: registers are
+// what limits a wave pair per SIMD, and three 16-byte reads per tile are cheap.
+constexpr int kQLds = 3, kQReg = 18 - kQLds;
+// Softmax reference margin (log2 domain): a tile whose maximum exceeds the
+// reference by more than this makes the workgroup run its segment again with
+// a larger reference; below it every weight and partial sum stays under 2^60.
+constexpr float kRescaleMargin = 60.0f;
+
+template <bool FP8>
+struct PairLds {
+  static constexpr int kCStage = Tile<false>::kStage + (FP8 ? 128 : 0);
+  static constexpr int kCStages = FP8 ? 2 : 3;
+  static constexpr int kRaw = kCStages * kCStage;              // first raw stage
+  static constexpr int kXchg = kRaw + (FP8 ? 3 * kRawStage : 0);
+  static constexpr int kQKeep = kXchg + 4 * kXchgSlot;  // per wave: the query fragments kept in LDS
+  static constexpr int kRestart = kQKeep + kPairWaves * kQLds * 1024;  // one restart word per pair
+  static constexpr int kPipe = kRestart + 16;
+  static constexpr int kBytes = kPipe > 4 * kQRegion ? kPipe : 4 * kQRegion;
+  static_assert(4 * 32 * kRowPitch <= kBytes, "output staging fits");
+  static_assert(kBytes <= 160 * 1024, "fits the LDS");
+};
+
+// One segment: a run of tiles [cb, ce) of unit (b, g); its rows go to out /
+// lse (final_out) or to partial rows starting at drow.
+struct PairSegment {
+  int b, g, L, cb, ce;
+  bool final_out;
+  int64_t drow;
+};
+
+// Direct HBM -> LDS loads of one bf16 tile by one role-1 wave (bw = 0..3):
+// latent rows bw + 4q (q < 8) and the rope of rows 8 bw .. 8 bw + 7.  Rows at
+// or past `valid` (slots past the request's end, which may hold anything) are
+// loaded from row valid - 1 instead: their scores are masked and their
+// weights are exactly 0, so a finite duplicate row contributes nothing.
+__device__ __forceinline__ void pair_issue_bf16(const char* tile_g, LDS_AS char* st, int bw, int valid) {
+  using G = Tile<false>;
+  const int lane = fresh_lane();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int r = bw + 4 * q;  // wave-uniform
+    const int rs = r < valid ? r : valid - 1;
+    lds_dma16(tile_g, rs * G::kRowBytes + 16 * lane, lds_addr(st + G::lat_base(r)));
+  }
+  const int r = 8 * bw + (lane >> 3);
+  const int rs = r < valid ? r : valid - 1;
+  const int c = (lane & 7) ^ G::xrope(r);
+  lds_dma16(tile_g, rs * G::kRowBytes + G::kLat + 16 * c, lds_addr(st + G::kLatBytes + 1024 * bw));
+}
+
+template <bool FP8, int ROLE>
+__device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* smem, const PairSegment& sg,
+                                             int pair, int tid) {
+  using G = Tile<false>;  // layout of the bf16 stages the MFMAs read
+  using Lds = PairLds<FP8>;
+  static_assert(!FP8, "E4M3 KV takes the four-wave kernel");
+  constexpr int kBase = 18 * ROLE;  // first 16-dim step of this wave's half of the dot
+  // Output columns: role 0 owns the 32-column blocks [0, 8), role 1 [8, 16).
+  constexpr int kNB = 8;               // 32-column output blocks of this wave
+  constexpr int kCol0 = ROLE ? 8 : 0;  // its first block
+  const int M = p.T * p.H;
+  const int b = sg.b, g = sg.g, L = sg.L, cb = sg.cb, ce = sg.ce;
+
+  // ---- query fragments: the pair stages its 32 rows through LDS with
+  // whole-row direct-to-LDS loads (role 0 latent rows 0..15, role 1 rows
+  // 16..31 and the rope rows), then each wave reads the fragments of its half
+  // of the dot.  Padding rows (gr >= M) reuse row M - 1 and are never written.
+  bf16x8 qf[kQReg];
+  {
+    LDS_AS char* qst = smem + pair * kQRegion;
+    LDS_AS char* qrs = qst + 32 * kRowPitch;
+    const int64_t qrow0 = (int64_t)b * M;
+    const int wr0 = g * kPairRows + 32 * pair;
+    const int ql = fresh_lane();
+#pragma unroll 4
+    for (int r = 16 * ROLE; r < 16 * ROLE + 16; ++r) {
+      const int rr = wr0 + r < M ? wr0 + r : M - 1;
+      lds_dma16((const char*)p.q_abs + (qrow0 + rr) * 1024, 16 * ql, lds_addr(qst + r * kRowPitch));
+    }
+    if (ROLE == 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rb = wr0 + 8 * j < M ? wr0 + 8 * j : M - 1;
+        const int rl = wr0 + 8 * j + (ql >> 3) < M ? wr0 + 8 * j + (ql >> 3) : M - 1;
+        lds_dma16((const char*)p.q_rope + (qrow0 + rb) * 128, (rl - rb) * 128 + 16 * (ql & 7),
+                  lds_addr(qrs + 1024 * j));
+      }
+    }
+    if (tid < 4) ((volatile LDS_AS uint32_t*)(smem + Lds::kRestart))[tid] = 0u;  // no restart requests yet
+    wait_vmcnt<0>();
+    __syncthreads();
+    const int ln = fresh_lane(), h = ln >> 5, n = ln & 31;
+    bf16x8 kept[kQLds];
+#pragma unroll
+    for (int s = 0; s < 18; ++s) {
+      const int kk = kBase + s;
+      const bf16x8 f = kk < 32 ? *(const LDS_AS bf16x8*)(qst + n * kRowPitch + 2 * (16 * kk + 8 * h))
+                               : *(const LDS_AS bf16x8*)(qrs + n * 128 + 2 * (16 * (kk - 32) + 8 * h));
+      if (s < kQReg) qf[s] = f;
+      else kept[s - kQReg] = f;
+    }
+    __syncthreads();  // every wave has its fragments before the stages refill
+    LDS_AS char* qkeep = smem + Lds::kQKeep + (pair + 4 * ROLE) * (kQLds * 1024);
+#pragma unroll
+    for (int j = 0; j < kQLds; ++j) *(LDS_AS bf16x8*)(qkeep + 1024 * j + 16 * ln) = kept[j];
+  }
+
+  floatx16 acc[kNB];
+  // role 0: softmax state of this lane's row.  p = 2^(s z - m_ref): m_ref is
+  // the first tile's maximum and never moves while accumulating, so neither
+  // wave ever rescales its accumulators.  A later tile maximum more than the
+  // margin above it makes the whole workgroup run the segment again with
+  // m_ref = the largest tile maximum seen (m_seen); real attention logits
+  // never do.  l: the normaliser share of this lane half.
+  float m_ref = neg_inf(), m_seen = neg_inf(), l_run = 0.0f;
+  int lim = 0;  // tokens >= lim are masked for this lane's row
+  if (ROLE == 0) {
+    const int gr = g * kPairRows + 32 * pair + (fresh_lane() & 31);
+    const int t = gr < M ? gr / p.H : 0;
+    const int vis = p.causal ? (L - p.T + 1 + t) : L;
+    lim = vis < ce ? vis : ce;
+  }
+  const float scale_log2 = p.scale * kLog2e;
+  const int ntiles = (ce - cb + 31) >> 5;
+  const char* kv = (const char*)p.kv;
+  const int xs_off = Lds::kXchg + pair * kXchgSlot;  // the pair's exchange slot
+  const int qk_off = Lds::kQKeep + (pair + 4 * ROLE) * (kQLds * 1024);
+
+  // The scores of the tile in st: this wave's 18 dot steps, one MFMA chain,
+  // key operands read from LDS two steps ahead.
+  auto scores = [&](const LDS_AS char* st, floatx16& S) {
+    const int ln = fresh_lane(), h = ln >> 5, n = ln & 31;
+    const int rho = swap_bits23(n);  // tile row feeding A-operand slot n
+    const LDS_AS char* kb = st + G::lat_base(rho) + 16 * h;
+    const LDS_AS char* rb = st + G::kLatBytes + rho * 128;
+    const int swr = G::xrope(rho);
+    const LDS_AS char* qk = smem + qk_off + 16 * ln;
+    auto kread = [&](int kk) -> bf16x8 {
+      return kk < 32 ? *(const LDS_AS bf16x8*)(kb + 32 * kk)
+                     : *(const LDS_AS bf16x8*)(rb + 16 * ((2 * (kk - 32) + h) ^ swr));
+    };
+    constexpr int KR = 2;
+    bf16x8 kring[KR], qk_reg[kQLds];
+#pragma unroll
+    for (int r = 0; r < KR; ++r) kring[r] = kread(kBase + r);
+#pragma unroll
+    for (int s = 0; s < 18; ++s) {
+      const bf16x8 a = kring[s % KR];
+      if (s + KR < 18) kring[s % KR] = kread(kBase + s + KR);
+      constexpr int kAhead = 4;  // kept fragments are read this many steps before use
+      if (s + kAhead >= kQReg && s + kAhead < 18) qk_reg[s + kAhead - kQReg] = *(const LDS_AS bf16x8*)(qk + 1024 * (s + kAhead - kQReg));
+      const bf16x8 q = s < kQReg ? qf[s < kQReg ? s : 0] : qk_reg[s < kQReg ? 0 : s - kQReg];
+      if (s == 0) mfma_v0(S, a, q);
+      else if (s < 17) mfma_v(S, a, q);
+      else mfma_v_last(S, a, q);
+      __builtin_amdgcn_sched_barrier(0);  // keep the operand rings as written
+    }
+  };
+  // This wave's half of the value product of the tile in sv with weights pw
+  // (token 16q + 8h + j of this lane's row in pw[q][j]).  The value operand
+  // of lane (lh, lsl) comes from rows r0 = 8 lh + (lsl >> 2) (+4, +16, +20)
+  // of the tile: B(r0 + 4) = B(r0) + 273 and B(r0 + 16) = B(r0) + 1088
+  // (r0 & 15 <= 11), so every read is one base register plus an immediate.
+  auto values = [&](const LDS_AS char* sv, const bf16x8 (&pw)[2]) {
+    const int ln = fresh_lane(), lh = ln >> 5, lsl = ln & 15, ldh = (ln >> 4) & 1;
+    const LDS_AS char* vb =
+        sv + G::lat_base(8 * lh + (lsl >> 2)) + 16 * (2 * ldh + ((lsl & 3) >> 1)) + 8 * (lsl & 1);
+    auto vread = [&](int x) -> bf16x8 {  // x: token half x / kNB, column block x % kNB
+      const LDS_AS char* b0 = vb + 16 * 1088 * (x / kNB) + 64 * (kCol0 + x % kNB);
+      const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)b0);
+      const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(b0 + 16 * 273));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int VR = 2;
+    bf16x8 vring[VR];
+#pragma unroll
+    for (int r = 0; r < VR; ++r) vring[r] = vread(r);
+#pragma unroll
+    for (int s = 0; s < 2 * kNB; ++s) {
+      const bf16x8 v = vring[s % VR];
+      if (s + VR < 2 * kNB) vring[s % VR] = vread(s + VR);
+      mfma_v(acc[s % kNB], v, pw[s / kNB]);
+    }
+  };
+  // Role 0, phase B: softmax of tile i from this wave's partial scores S and
+  // the partner's (from the slot); writes the bf16 weights to the slot.
+  auto softmax = [&](auto with_mask, floatx16& S, int i, bf16x8 (&pw)[2]) {
+    constexpr bool kMask = decltype(with_mask)::value;
+    const int ln = fresh_lane();
+    const LDS_AS char* xs = smem + xs_off + 16 * ln;
+    // token 16 (e >> 3) + 8 h + (e & 7) is visible iff 16 (e >> 3) + (e & 7)
+    // < lim - (cb + 32 i) - 8 h: one bound, compared against immediates
+    const int lim_h = lim - (cb + 32 * i) - 8 * (ln >> 5);
+    float mx_a = neg_inf(), mx_b = neg_inf();
+    // (four scores at a time, each group its own scheduling region, so that
+    // few temporaries are live next to the accumulators)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const floatx4 sb = *(const LDS_AS floatx4*)(xs + 1024 * k);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = 4 * k + c;
+        float v = S[e] + sb[c];
+        if constexpr (kMask) v = 16 * (e >> 3) + (e & 7) < lim_h ? v : neg_inf();
+        S[e] = v;
+        if (e & 1) mx_b = __builtin_fmaxf(mx_b, v);
+        else mx_a = __builtin_fmaxf(mx_a, v);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // row maximum (both lane halves), times s = scale * log2 e > 0
+    const float mx = half_swap_max(__builtin_fmaxf(mx_a, mx_b)) * scale_log2;
+    if (m_ref == neg_inf()) m_ref = mx;  // first tile with a visible token: nothing accumulated yet
+    m_seen = __builtin_fmaxf(m_seen, mx);
+    // a maximum past the margin asks for a run with a larger reference (read
+    // by every wave after the next barrier); this tile's weights are then unused
+    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleMargin) != 0 && ln == 0)
+      *(volatile LDS_AS uint32_t*)(smem + Lds::kRestart + 4 * (xs_off - Lds::kXchg) / kXchgSlot) = 1u;
+    const float mu = m_ref == neg_inf() ? 0.0f : m_ref;
+    float la = 0.0f, lb = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const __bf16 w0 = (__bf16)fast_exp2(__builtin_fmaf(S[e], scale_log2, -mu));
+      const __bf16 w1 = (__bf16)fast_exp2(__builtin_fmaf(S[e + 1], scale_log2, -mu));
+      la += (float)w0;  // the normaliser sums the weights as the value product sees them
+      lb += (float)w1;
+      pw[e >> 3][e & 7] = w0;
+      pw[e >> 3][(e & 7) + 1] = w1;
+      if (e % 4 == 2) __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += la + lb;
+    // slot: weights [0, 2048) (the partner's partial scores there were read above)
+    LDS_AS char* xw = smem + xs_off + 16 * ln;
+    *(LDS_AS bf16x8*)xw = pw[0];
+    *(LDS_AS bf16x8*)(xw + 1024) = pw[1];
+  };
+
+  // ---- the tile loop.  Step i: phase A scores tile i (role 1 also issues the
+  // loads of tile i + 1, into the stage tile i - 2 left, and hands over its
+  // partial scores); phase B: role 0 runs the softmax of tile i and its half
+  // of tile i's value product while role 1 runs its half of tile i - 1's.
+  auto tile_g = [&](int i) {
+    return kv + kv_row_index<true>(p.page_table, p.MP, p.P, b, cb + 32 * i) * G::kRowBytes;
+  };
+  for (;;) {  // once, unless a tile asks for a larger softmax reference
+#pragma unroll
+    for (int db = 0; db < kNB; ++db) acc[db] = floatx16{};
+    l_run = 0.0f;
+    if (ROLE == 1 && 0 < ntiles) pair_issue_bf16(tile_g(0), smem, pair, L - cb);
+    int so_cur = 0;  // stage offsets of tiles i and i - 1 (three stages, rotating)
+    int so_prev = 2 * Lds::kCStage;
+    bool restart = false;
+    for (int i = 0; i <= ntiles; ++i) {
+      if (ROLE == 1) wait_vmcnt<0>();  // tile i has landed
+      __syncthreads();  // tile i is in its stage; every wave is done with step i - 1
+      {  // requests made by the softmax of tile i - 1 (no load is in flight here)
+        const uintx4 rq = *(const LDS_AS uintx4*)(smem + Lds::kRestart);
+        if (__builtin_amdgcn_readfirstlane((int)(rq[0] | rq[1] | rq[2] | rq[3])) != 0) {
+          restart = true;
+          break;
+        }
+      }
+      const int so_next = so_cur == 2 * Lds::kCStage ? 0 : so_cur + Lds::kCStage;
+      // (initialised here so that it is not carried from step to step)
+      bf16x8 pw[2] = {bf16x8{}, bf16x8{}};  // role 0: the weights of tile i; role 1: those of tile i - 1
+      if (ROLE == 1) {
+        if (i + 1 < ntiles) pair_issue_bf16(tile_g(i + 1), smem + so_next, pair, L - (cb + 32 * (i + 1)));
+        if (i >= 1) {  // the weights of tile i - 1
+          const int ln = fresh_lane();
+          pw[0] = *(const LDS_AS bf16x8*)(smem + xs_off + 16 * ln);
+          pw[1] = *(const LDS_AS bf16x8*)(smem + xs_off + 1024 + 16 * ln);
+        }
+      }
+      floatx16 S = __builtin_nondeterministic_value(S);  // defined by the scores when used
+      if (i < ntiles) {
+        scores(smem + so_cur, S);
+        if (ROLE == 1) {
+          LDS_AS char* xw = smem + xs_off + 16 * fresh_lane();
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            *(LDS_AS floatx4*)(xw + 1024 * k) = floatx4{S[4 * k], S[4 * k + 1], S[4 * k + 2], S[4 * k + 3]};
+        }
+      }
+      __syncthreads();  // the partial scores are in the slots
+      if (ROLE == 0) {
+        if (i == ntiles) break;
+        const bool full = __builtin_amdgcn_ballot_w64(lim - (cb + 32 * i) < 32) == 0;
+        if (__builtin_amdgcn_readfirstlane((int)full))
+          softmax(std::false_type{}, S, i, pw);
+        else
+          softmax(std::true_type{}, S, i, pw);
+        __builtin_amdgcn_sched_barrier(0);
+        values(smem + so_cur, pw);
+      } else {
+        if (i >= 1) values(smem + so_prev, pw);
+        if (i == ntiles) break;
+      }
+      so_prev = so_cur;
+      so_cur = so_next;
+    }
+    if (!restart) break;
+    // rare path: every wave has read the requests before they are cleared;
+    // the next run starts with the largest maximum seen as its reference
+    mfma_drain();  // no value MFMA still writes the accumulators zeroed next
+    __syncthreads();
+    if (tid < 4) ((volatile LDS_AS uint32_t*)(smem + Lds::kRestart))[tid] = 0u;
+    m_ref = m_seen;
+  }
+
+  // ---- epilogue: role 0 forms 1 / normaliser and lse and hands 1 / l to role 1
+  mfma_drain();  // the last value MFMAs' results are in the accumulators
+  int pr = pair;
+  asm volatile("" : "+s"(pr));  // recomputed here, not kept through the loop
+  const int ln = fresh_lane(), h = ln >> 5, n = ln & 31;
+  LDS_AS char* xe = smem + Lds::kXchg + pr * kXchgSlot + 2304 + 4 * ln;
+  float inv = 0.0f, lse_v = neg_inf();
+  if (ROLE == 0) {
+    const float l_tot = half_swap_sum(l_run);
+    inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    lse_v = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : neg_inf();
+    *(LDS_AS float*)xe = inv;
+  }
+  __syncthreads();
+  if (ROLE == 1) inv = *(const LDS_AS float*)xe;
+  int64_t drow = sg.drow;
+  asm volatile("" : "+s"(drow));
+  __syncthreads();  // the slots are read before the staging below overwrites them
+
+  // The pair's rows go out through LDS: each wave writes its normalised
+  // columns of the 32 rows at pitch kRowPitch, then each wave stores 16 whole
+  // rows (role 0 rows 0..15, role 1 rows 16..31), 1 KB per store.
+  LDS_AS char* wst = smem + pr * 32 * kRowPitch;
+  const int wrow0 = g * kPairRows + 32 * pr;  // unit row of staged row 0
+  auto stage_bf16 = [&]() {
+#pragma unroll
+    for (int db = 0; db < kNB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const floatx4 v = floatx4{acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]} * inv;
+        *(LDS_AS bf16x4*)(wst + n * kRowPitch + 2 * (32 * (kCol0 + db) + 8 * g4 + 4 * h)) =
+            bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+      }
+  };
+  auto stage_f32 = [&](int half) {  // this wave's blocks among columns [256 half, 256 half + 256)
+#pragma unroll
+    for (int db = 0; db < kNB; ++db) {
+      const int cb32 = kCol0 + db - 8 * half;
+      if (cb32 < 0 || cb32 >= 8) continue;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const floatx4 v = floatx4{acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]} * inv;
+        *(LDS_AS floatx4*)(wst + n * kRowPitch + 4 * (32 * cb32 + 8 * g4 + 4 * h)) = v;
+      }
+    }
+  };
+  auto drain = [&](char* dst, int64_t row_bytes) {  // dst: staged row 0's destination
+#pragma unroll 1
+    for (int r0 = 16 * ROLE; r0 < 16 * ROLE + 16; r0 += 8) {
+      uintx4 v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = *(const LDS_AS uintx4*)(wst + (r0 + r) * kRowPitch + 16 * ln);
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (wrow0 + r0 + r < M) *(uintx4*)(dst + (r0 + r) * row_bytes + 16 * ln) = v[r];
+    }
+  };
+  const int64_t orow0 = drow + 32 * pr;
+  if (sg.final_out && p.out_dtype == kBF16) {
+    stage_bf16();
+    __syncthreads();
+    drain((char*)((__bf16*)p.out + orow0 * 512), 1024);
+  } else if (!sg.final_out && p.NB > 0) {  // balanced slots hold bf16 partials
+    stage_bf16();
+    __syncthreads();
+    drain((char*)((__bf16*)p.part_o + orow0 * 512), 1024);
+  } else {
+    float* base = sg.final_out ? (float*)p.out + orow0 * 512 : p.part_o + orow0 * 512;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      stage_f32(pass);
+      __syncthreads();
+      drain((char*)(base + 256 * pass), 2048);
+      __syncthreads();
+    }
+  }
+  if (ROLE == 0 && h == 0 && wrow0 + n < M) {
+    const int64_t orow = drow + 32 * pr + n;
+    if (!sg.final_out) p.part_lse[orow] = lse_v;
+    else if (p.lse) p.lse[orow] = lse_v;
+  }
+}
+
+template <bool FP8>
+__global__ void __launch_bounds__(64 * kPairWaves, 1)
+mla_split_pair(SplitParams p, int groups) {
+  using Lds = PairLds<FP8>;
+  constexpr int kWaves = kPairWaves;
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+  LDS_AS char* smem = (LDS_AS char*)(LDS_AS void*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int pair = wave & 3, role = wave >> 2;
+
+  // Work of this workgroup: a list of segments, each a run of 32-token tiles
+  // of one unit (request b, row group g).
+  //   Uniform chunks (p.NB == 0): one segment, chunk s of unit (b, g).  The
+  //   block mapping is XCD-aware: consecutive hardware block ids go to
+  //   different XCDs (id mod 8), so the row groups of one (request, chunk)
+  //   are given ids 8 apart and share that XCD's L2 while they read the same
+  //   pages.
+  //   Balanced (p.NB > 0): the units' tiles, laid end to end (unit-major,
+  //   each unit's preceded by kUnitStartCost positions for the cost of
+  //   starting it; prefix sums in p.tile_prefix), are cut into NB equal
+  //   contiguous ranges, one per workgroup; a range crosses unit boundaries
+  //   freely, so every workgroup gets the same work whatever the length mix,
+  //   a workgroup that starts a unit inside its range that many tiles fewer.
+  int ub = 0, ug = 0, us = 0;
+  int wx = 0, wx1 = 0;
+  int wu = 0, wk = 0, wsu = 0;  // balanced: current unit and its first position
+  if (p.NB == 0 && p.Sp > 0) {
+    // Cascade: chunk s runs on XCD s mod 8, where its workgroups for every
+    // request and row group take consecutive slots, so that the workgroups
+    // reading one shared-prefix chunk run together and share that XCD's L2.
+    const int x = blockIdx.x;
+    const int xcd = x & 7, slot = x >> 3;
+    const int per = p.B * groups;
+    const int sl8 = slot / per, rem = slot - sl8 * per;
+    us = 8 * sl8 + xcd;
+    if (us >= p.S) return;
+    ub = rem / groups;
+    ug = rem - ub * groups;
+  } else if (p.NB == 0) {
+    const int x = blockIdx.x;
+    const int xcd = x & 7, slot = x >> 3;
+    const int k8 = slot / groups;
+    ug = slot - k8 * groups;
+    const int unit = 8 * k8 + xcd;
+    if (unit >= p.B * p.S) return;
+    ub = unit / p.S;
+    us = unit - ub * p.S;
+  } else {
+    // Plan, in every workgroup: each thread sums the positions of a run of
+    // units, a block-wide scan gives the runs' offsets, and the thread whose
+    // run holds this workgroup's first position finds its unit.  Workgroup 0
+    // also writes the prefix sums for the merge.  (The scratch words sit in
+    // the exchange slots, unused until the first tile.)
+    volatile LDS_AS int* ps = (volatile LDS_AS int*)(smem + Lds::kXchg);
+    const int U = p.B * groups;
+    const int per = (U + 64 * kWaves - 1) / (64 * kWaves);
+    const int u0 = tid * per < U ? tid * per : U;
+    const int u1 = u0 + per < U ? u0 + per : U;
+    auto unit_tiles = [&](int u) {  // the unit's positions: tiles + start cost
+      const int Lu = p.seq_lens[u / groups];
+      return Lu > 0 ? ((Lu + 31) >> 5) + kUnitStartCost : 0;
+    };
+    int run_sum = 0;
+    for (int u = u0; u < u1; ++u) run_sum += unit_tiles(u);
+    int incl = run_sum;  // inclusive scan within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) ps[wave] = incl;
+    __syncthreads();
+    int W = 0, before = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int v = ps[w];
+      before += w < wave ? v : 0;
+      W += v;
+    }
+    W = __builtin_amdgcn_readfirstlane(W);  // the same in every lane
+    const int excl = before + incl - run_sum;
+    if (blockIdx.x == 0) {
+      int run = excl;
+      for (int u = u0; u < u1; ++u) {
+        p.tile_prefix[u] = run;
+        run += unit_tiles(u);
+      }
+      if (tid == 0) p.tile_prefix[U] = W;
+    }
+    // no workgroup with an empty range (a range may still hold only a unit's
+    // start positions: its workgroup then has no segment)
+    const int64_t nb = W < p.NB ? W : p.NB;
+    // Ranges are dealt so that each XCD (hardware block id mod 8; the grid
+    // is NB workgroups) runs a contiguous run of NB / 8 of them: the few
+    // workgroups that share a unit, and so read its query rows, mostly share
+    // one L2.
+    wk = (p.NB & 7) == 0 ? (int)(blockIdx.x & 7) * (p.NB >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+    if (wk >= nb) return;
+    // (W < 2^30, so the bounds fit in int32; read back as wave-uniform values)
+    wx = __builtin_amdgcn_readfirstlane((int)(wk * (int64_t)W / nb));
+    wx1 = __builtin_amdgcn_readfirstlane((int)((wk + 1) * (int64_t)W / nb));
+    if (excl <= wx && wx < excl + run_sum) {
+      int run = excl, fu = u0, fr = excl;
+      bool found = false;
+      for (int u = u0; u < u1; ++u) {
+        const int tu = unit_tiles(u);
+        const bool hit = !found && wx < run + tu;
+        fu = hit ? u : fu;
+        fr = hit ? run : fr;
+        found = found || hit;
+        run += tu;
+      }
+      ps[kWaves] = fu;
+      ps[kWaves + 1] = fr;
+    }
+    __syncthreads();
+    wu = __builtin_amdgcn_readfirstlane(ps[kWaves]);
+    wsu = __builtin_amdgcn_readfirstlane(ps[kWaves + 1]);
+  }
+
+  const int M = p.T * p.H;
+  for (bool more_segments = true; more_segments;) {
+    PairSegment sg;
+    if (p.NB == 0) {
+      more_segments = false;
+      sg.b = ub;
+      sg.g = ug;
+      sg.L = uniform_load(p.seq_lens + ub);
+      if (p.Sp == 0) {
+        chunk_span(sg.L, p.S, p.P, us, &sg.cb, &sg.ce);
+      } else if (us < p.Sp) {  // shared-prefix chunk: the same bounds for every request
+        chunk_span(p.prefix_len, p.Sp, p.P, us, &sg.cb, &sg.ce);
+        sg.cb = sg.cb < sg.L ? sg.cb : sg.L;
+        sg.ce = sg.ce < sg.L ? sg.ce : sg.L;
+      } else {  // suffix chunk of [prefix_len, L)
+        const int Ls = sg.L > p.prefix_len ? sg.L - p.prefix_len : 0;
+        chunk_span(Ls, p.S - p.Sp, p.P, us - p.Sp, &sg.cb, &sg.ce);
+        sg.cb += p.prefix_len;
+        sg.ce += p.prefix_len;
+      }
+      sg.final_out = p.write_final;
+      sg.drow = sg.final_out ? (int64_t)ub * M + (int64_t)ug * kPairRows
+                             : ((int64_t)ub * p.S + us) * M + (int64_t)ug * kPairRows;
+    } else {
+      // Unit wu occupies positions [su, eu): kUnitStartCost positions, then
+      // its tiles from ts = su + kUnitStartCost on.
+      int su = wsu, eu, L, b;
+      for (;;) {  // skip units that end at or before wx (and units without tiles)
+        b = wu / groups;
+        L = uniform_load(p.seq_lens + b);
+        eu = su + (L > 0 ? ((L + 31) >> 5) + kUnitStartCost : 0);
+        if (eu > wx) break;
+        ++wu;
+        su = eu;
+      }
+      const int ts = su + kUnitStartCost;
+      const int s0 = wx > ts ? (int)wx : ts;
+      const int e = (int)(wx1 < eu ? wx1 : eu);
+      if (s0 >= e) break;  // the range ends inside the unit's start cost: none of its tiles here
+      sg.b = b;
+      sg.L = L;
+      sg.g = wu - b * groups;
+      sg.cb = 32 * (s0 - ts);
+      sg.ce = 32 * (e - ts);
+      if (sg.ce > L) sg.ce = L;
+      // Partial slots: [NB][2][kPairRows] rows.  Slot 0 holds the segment that
+      // continues a unit begun in an earlier workgroup, slot 1 the one that
+      // starts a unit and continues into later workgroups.
+      sg.final_out = s0 == ts && e == eu;
+      sg.drow = sg.final_out ? (int64_t)b * M + (int64_t)sg.g * kPairRows
+                             : ((int64_t)wk * 2 + (s0 > ts ? 0 : 1)) * kPairRows;
+      wx = e;
+      ++wu;
+      wsu = eu;
+      more_segments = wx < wx1;
+    }
+    // the previous segment's waves are done with all of the LDS
+    __syncthreads();
+    if (role == 0)
+      pair_segment<FP8, 0>(p, smem, sg, pair, tid);
+    else
+      pair_segment<FP8, 1>(p, smem, sg, pair, tid);
+  }
+}
+
+template <bool FP8>
+hipError_t launch_pair(const SplitParams& p, hipStream_t stream) {
+  const int M = p.T * p.H;
+  const int groups = (M + kPairRows - 1) / kPairRows;
+  static_assert(kPairRows == kBalancedRows, "balanced units are one workgroup of rows");
+  const int units = p.B * p.S;
+  const int64_t blocks = p.NB > 0   ? (int64_t)p.NB
+                         : p.Sp > 0 ? 8LL * ((p.S + 7) / 8) * p.B * groups  // cascade: chunk-major per XCD
+                                    : 8LL * groups * ((units + 7) / 8);
+  const size_t lds = (size_t)PairLds<FP8>::kBytes;
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute((const void*)mla_split_pair<FP8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)lds);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((mla_split_pair<FP8>), dim3((unsigned)blocks), dim3(64 * kPairWaves), lds, stream, p,
+                     groups);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------- generic split kernel
@@ -1925,8 +2570,10 @@ Kernel pick_kernel(const SplitParams& p) {
 }
 
 hipError_t launch_split(const SplitParams& p, hipStream_t stream) {
+  const char* sel = getenv("MLA_MFMA_KERNEL");
+  const bool four = sel && sel[0] == 'f';
   switch (pick_kernel(p)) {
-    case Kernel::kMfmaBf16: return launch_mfma<false, 4, 4>(p, stream);
+    case Kernel::kMfmaBf16: return four ? launch_mfma<false, 4, 4>(p, stream) : launch_pair<false>(p, stream);
     case Kernel::kMfmaFp8: return launch_mfma<true, 4, 8>(p, stream);
     default: break;
   }
