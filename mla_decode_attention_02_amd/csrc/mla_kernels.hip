@@ -20,6 +20,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -56,12 +57,18 @@ __device__ __forceinline__ T uniform_load(const T* p) {
 // it ("推理优化" tag page, PagedAttention article).  The decode kernels and the
 // gather hook resolve rows through this routine; kUniform reads the table
 // entry through the scalar cache (b and j the same in every lane).
+// (kv_page_entry and kv_row_of_page are its two halves, for callers that
+// read the entry ahead of its use.)
+__device__ __forceinline__ const int32_t* kv_page_entry(const int32_t* __restrict__ page_table, int MP,
+                                                        int P, int b, int j) {
+  return page_table + (int64_t)b * MP + j / P;
+}
+__device__ __forceinline__ int64_t kv_row_of_page(int page, int P, int j) { return (int64_t)page * P + (j % P); }
 template <bool kUniform = false>
 __device__ __forceinline__ int64_t kv_row_index(const int32_t* __restrict__ page_table, int MP,
                                                 int P, int b, int j) {
-  const int32_t* entry = page_table + (int64_t)b * MP + j / P;
-  const int page = kUniform ? uniform_load(entry) : *entry;
-  return (int64_t)page * P + (j % P);
+  const int32_t* entry = kv_page_entry(page_table, MP, P, b, j);
+  return kv_row_of_page(kUniform ? uniform_load(entry) : *entry, P, j);
 }
 
 // Split plan: chunk k of a request of length L, with S chunks, covers
@@ -607,11 +614,11 @@ mla_split_mfma(SplitParams p, int groups) {
 
   const char* kv = (const char*)p.kv;
   const int rho = swap_bits23(n);  // tile row feeding A-operand slot n
-  const int64_t pt_row = (int64_t)b * p.MP;
 
   auto stage_of = [&](int i) -> LDS_AS char* { return smem + (i % STAGES) * G::kStage; };
-  auto page_of = [&](int i) { return uniform_load(p.page_table + pt_row + (cb + 32 * i) / p.P); };
-  auto row_of = [&](int i, int page) { return (int64_t)page * p.P + ((cb + 32 * i) % p.P); };
+  // the two halves of kv_row_index, the entry read a step ahead of its use
+  auto page_of = [&](int i) { return uniform_load(kv_page_entry(p.page_table, p.MP, p.P, b, cb + 32 * i)); };
+  auto row_of = [&](int i, int page) { return kv_row_of_page(page, p.P, cb + 32 * i); };
   auto issue = [&](int i) {
     const int64_t row0 = row_of(i, page_of(i));
     issue_tile<FP8, WAVES>(kv + row0 * G::kRowBytes, FP8 ? p.kv_scales + row0 : nullptr,
@@ -905,8 +912,7 @@ mla_split_mfma(SplitParams p, int groups) {
       pprev[0] = pcur[0];
       pprev[1] = pcur[1];
       // branch-free: past the last tile this re-reads a valid entry and is unused
-      pg_next = uniform_load(p.page_table + pt_row +
-                             (i + kDepth + 1 < ntiles ? (cb + 32 * (i + kDepth + 1)) / p.P : 0));
+      pg_next = page_of(i + kDepth + 1 < ntiles ? i + kDepth + 1 : 0);
     }
     if (!restart) break;
     // Rare path: drain the pipeline, reset, and run the chunk again (the
@@ -995,37 +1001,31 @@ mla_split_mfma(SplitParams p, int groups) {
 }
 
 // --------------------------------------------- MFMA split kernel, wave pairs
-// One workgroup = 8 wavefronts = the 128 query rows of one unit (request b,
-// row group g; row r = t * H + h, the query-token fold), as four pairs: pair
-// p (waves p and p + 4) owns rows 32p .. 32p + 31.  The pair splits both
-// contractions in halves: wave p (role 0) forms the partial scores over dims
-// [0, 288) of the 576-deep dot and owns output columns [0, 256); wave p + 4
-// (role 1) takes dims [288, 576) and columns [256, 512).  A wave so holds 72
-// query registers and 128 accumulators, and two waves share each SIMD: one
-// issues while the other waits.
+// One workgroup = NP pairs of wavefronts (NP = 4: 8 waves, 128 query rows,
+// the unit of the balanced work list; NP = 2: 4 waves, 64 rows, for uniform
+// plans that would otherwise leave compute units idle) over rows of one
+// request b (row r = t * H + h, the query-token fold).  Pair p (waves p and
+// p + NP) owns rows 32p .. 32p + 31 of the workgroup and splits both
+// contractions in halves: role 0 (wave p + NP) forms the partial scores over
+// dims [0, 288) of the 576-deep dot and owns output columns [0, 256); role 1
+// (wave p) takes dims [288, 576) and columns [256, 512).  A wave so
+// holds 15 query fragments in registers (3 more in LDS) and 128 fp32
+// accumulators, 252 VGPRs in all: with NP = 4 two waves share each SIMD.
 //
 // Scores are S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (a row's 32 token
 // scores sit in one lane pair), values O^T += V^T P^T with V read transposed
-// from the same LDS tile.  Per tile i (32 tokens), in two phases:
-//   phase 1  both waves score tile i (18 MFMAs, one chain) interleaved with
-//            their half of the value product of tile i - 1 (16 MFMAs); role 1
-//            writes its partial score tile to the pair's LDS slot;
-//   barrier
-//   phase 2  role 0 adds the partial, runs the softmax of tile i and writes
-//            the bf16 weights and the rescale factor to the slot; role 1
-//            refills the stage freed by tile i - 1 (bf16 KV: tile i + 2 by
-//            direct HBM -> LDS loads) or converts the next FP8 tile to bf16
-//            (E4M3 KV: raw tiles are loaded three ahead, each converted once
-//            for the whole workgroup);
-//   barrier.
-// LDS: bf16 KV -- three tile stages; E4M3 KV -- two bf16 stages of converted
-// tiles (plus their 32 token scales) and three raw E4M3 stages; and four 4 KB
-// exchange slots (role 1's partial scores, then role 0's weights, rescale
-// factors and, at the end, 1 / normaliser).
-constexpr int kPairWaves = 8;
-constexpr int kPairRows = 32 * 4;
-constexpr int kRawTileBytes = 32 * 576;          // E4M3 codes of one tile
-constexpr int kRawStage = kRawTileBytes + 1024;  // + the 32 scales, 8 copies
+// from the same LDS tile.  Step i (tile i, 32 tokens), one workgroup barrier:
+//   role 1  issues the direct HBM -> LDS loads of tile i + 1 (its share of
+//           the tile; the stage tile i - 2 left), scores tile i (18 MFMAs,
+//           one chain), writes its partial score tile to the pair's LDS slot
+//           and marks it ready, then runs its half of tile i - 1's value
+//           product (16 MFMAs) with the weights role 0 left in the slot;
+//   role 0  scores tile i, waits for the mark, adds the partial, runs the
+//           softmax (lazy reference, see kRescaleMargin), writes the bf16
+//           weights to the slot and runs its half of tile i's value product.
+// LDS: three bf16 tile stages, one 4 KB exchange slot per pair (partial
+// scores, then weights, at the end 1 / normaliser), the kept query
+// fragments, one restart word and one ready mark per pair.
 constexpr int kXchgSlot = 4096;
 constexpr int kRowPitch = 1024 + 16;             // staged query / output rows
 constexpr int kQRegion = 32 * kRowPitch + 32 * 128;
@@ -1038,17 +1038,17 @@ constexpr int kQLds = 3, kQReg = 18 - kQLds;
 // a larger reference; below it every weight and partial sum stays under 2^60.
 constexpr float kRescaleMargin = 60.0f;
 
-template <bool FP8>
+template <int NP>
 struct PairLds {
-  static constexpr int kCStage = Tile<false>::kStage + (FP8 ? 128 : 0);
-  static constexpr int kCStages = FP8 ? 2 : 3;
-  static constexpr int kRaw = kCStages * kCStage;              // first raw stage
-  static constexpr int kXchg = kRaw + (FP8 ? 3 * kRawStage : 0);
-  static constexpr int kQKeep = kXchg + 4 * kXchgSlot;  // per wave: the query fragments kept in LDS
-  static constexpr int kRestart = kQKeep + kPairWaves * kQLds * 1024;  // one restart word per pair
-  static constexpr int kPipe = kRestart + 16;
-  static constexpr int kBytes = kPipe > 4 * kQRegion ? kPipe : 4 * kQRegion;
-  static_assert(4 * 32 * kRowPitch <= kBytes, "output staging fits");
+  static_assert(NP == 2 || NP == 4, "two or four pairs per workgroup");
+  static constexpr int kCStage = Tile<false>::kStage;
+  static constexpr int kXchg = 3 * kCStage;             // exchange slots, one per pair
+  static constexpr int kQKeep = kXchg + NP * kXchgSlot;  // per wave: the query fragments kept in LDS
+  static constexpr int kRestart = kQKeep + 2 * NP * kQLds * 1024;  // one restart word per pair (4 words)
+  static constexpr int kReady = kRestart + 16;  // per pair: tiles whose partial scores are in the slot
+  static constexpr int kPipe = kReady + 16;
+  static constexpr int kBytes = kPipe > NP * kQRegion ? kPipe : NP * kQRegion;
+  static_assert(NP * 32 * kRowPitch <= kBytes, "output staging fits");
   static_assert(kBytes <= 160 * 1024, "fits the LDS");
 };
 
@@ -1060,32 +1060,42 @@ struct PairSegment {
   int64_t drow;
 };
 
-// Direct HBM -> LDS loads of one bf16 tile by one role-1 wave (bw = 0..3):
-// latent rows bw + 4q (q < 8) and the rope of rows 8 bw .. 8 bw + 7.  Rows at
-// or past `valid` (slots past the request's end, which may hold anything) are
+// Direct HBM -> LDS loads of one bf16 tile by role-1 wave bw (0 .. NP - 1),
+// kPairLoads<NP> of them: load k < 32 / NP is latent row bw + NP k, the rest
+// the rope of the 8-row groups c = bw + NP j (rows 8c .. 8c + 7).  Rows at or
+// past `valid` (slots past the request's end, which may hold anything) are
 // loaded from row valid - 1 instead: their scores are masked and their
 // weights are exactly 0, so a finite duplicate row contributes nothing.
-__device__ __forceinline__ void pair_issue_bf16(const char* tile_g, LDS_AS char* st, int bw, int valid) {
+template <int NP>
+constexpr int kPairLoads = 32 / NP + 4 / NP;
+template <int NP>
+__device__ __forceinline__ void pair_issue_piece(const char* tile_g, LDS_AS char* st, int bw, int valid, int k) {
   using G = Tile<false>;
   const int lane = fresh_lane();
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int r = bw + 4 * q;  // wave-uniform
+  if (k < 32 / NP) {
+    const int r = bw + NP * k;  // wave-uniform
     const int rs = r < valid ? r : valid - 1;
     lds_dma16(tile_g, rs * G::kRowBytes + 16 * lane, lds_addr(st + G::lat_base(r)));
+  } else {
+    const int c8 = bw + NP * (k - 32 / NP);
+    const int r = 8 * c8 + (lane >> 3);
+    const int rs = r < valid ? r : valid - 1;
+    const int c = (lane & 7) ^ G::xrope(r);
+    lds_dma16(tile_g, rs * G::kRowBytes + G::kLat + 16 * c, lds_addr(st + G::kLatBytes + 1024 * c8));
   }
-  const int r = 8 * bw + (lane >> 3);
-  const int rs = r < valid ? r : valid - 1;
-  const int c = (lane & 7) ^ G::xrope(r);
-  lds_dma16(tile_g, rs * G::kRowBytes + G::kLat + 16 * c, lds_addr(st + G::kLatBytes + 1024 * bw));
+}
+template <int NP>
+__device__ __forceinline__ void pair_issue_bf16(const char* tile_g, LDS_AS char* st, int bw, int valid) {
+#pragma unroll
+  for (int k = 0; k < kPairLoads<NP>; ++k) pair_issue_piece<NP>(tile_g, st, bw, valid, k);
 }
 
-template <bool FP8, int ROLE>
+template <int NP, int ROLE>
 __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* smem, const PairSegment& sg,
                                              int pair, int tid) {
   using G = Tile<false>;  // layout of the bf16 stages the MFMAs read
-  using Lds = PairLds<FP8>;
-  static_assert(!FP8, "E4M3 KV takes the four-wave kernel");
+  using Lds = PairLds<NP>;
+  constexpr int kRows = 32 * NP;  // rows of a workgroup
   constexpr int kBase = 18 * ROLE;  // first 16-dim step of this wave's half of the dot
   // Output columns: role 0 owns the 32-column blocks [0, 8), role 1 [8, 16).
   constexpr int kNB = 8;               // 32-column output blocks of this wave
@@ -1102,7 +1112,7 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
     LDS_AS char* qst = smem + pair * kQRegion;
     LDS_AS char* qrs = qst + 32 * kRowPitch;
     const int64_t qrow0 = (int64_t)b * M;
-    const int wr0 = g * kPairRows + 32 * pair;
+    const int wr0 = g * kRows + 32 * pair;
     const int ql = fresh_lane();
 #pragma unroll 4
     for (int r = 16 * ROLE; r < 16 * ROLE + 16; ++r) {
@@ -1118,7 +1128,7 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
                   lds_addr(qrs + 1024 * j));
       }
     }
-    if (tid < 4) ((volatile LDS_AS uint32_t*)(smem + Lds::kRestart))[tid] = 0u;  // no restart requests yet
+    if (tid < 8) ((volatile LDS_AS uint32_t*)(smem + Lds::kRestart))[tid] = 0u;  // no requests, no scores yet
     wait_vmcnt<0>();
     __syncthreads();
     const int ln = fresh_lane(), h = ln >> 5, n = ln & 31;
@@ -1132,7 +1142,7 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
       else kept[s - kQReg] = f;
     }
     __syncthreads();  // every wave has its fragments before the stages refill
-    LDS_AS char* qkeep = smem + Lds::kQKeep + (pair + 4 * ROLE) * (kQLds * 1024);
+    LDS_AS char* qkeep = smem + Lds::kQKeep + (pair + NP * ROLE) * (kQLds * 1024);
 #pragma unroll
     for (int j = 0; j < kQLds; ++j) *(LDS_AS bf16x8*)(qkeep + 1024 * j + 16 * ln) = kept[j];
   }
@@ -1147,7 +1157,7 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
   float m_ref = neg_inf(), m_seen = neg_inf(), l_run = 0.0f;
   int lim = 0;  // tokens >= lim are masked for this lane's row
   if (ROLE == 0) {
-    const int gr = g * kPairRows + 32 * pair + (fresh_lane() & 31);
+    const int gr = g * kRows + 32 * pair + (fresh_lane() & 31);
     const int t = gr < M ? gr / p.H : 0;
     const int vis = p.causal ? (L - p.T + 1 + t) : L;
     lim = vis < ce ? vis : ce;
@@ -1156,7 +1166,8 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
   const int ntiles = (ce - cb + 31) >> 5;
   const char* kv = (const char*)p.kv;
   const int xs_off = Lds::kXchg + pair * kXchgSlot;  // the pair's exchange slot
-  const int qk_off = Lds::kQKeep + (pair + 4 * ROLE) * (kQLds * 1024);
+  const int pr_slot = pair;
+  const int qk_off = Lds::kQKeep + (pair + NP * ROLE) * (kQLds * 1024);
 
   // The scores of the tile in st: this wave's 18 dot steps, one MFMA chain,
   // key operands read from LDS two steps ahead.
@@ -1171,7 +1182,7 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
       return kk < 32 ? *(const LDS_AS bf16x8*)(kb + 32 * kk)
                      : *(const LDS_AS bf16x8*)(rb + 16 * ((2 * (kk - 32) + h) ^ swr));
     };
-    constexpr int KR = 2;
+    constexpr int KR = ROLE ? 3 : 2;  // role 1 has the registers for a deeper ring
     bf16x8 kring[KR], qk_reg[kQLds];
 #pragma unroll
     for (int r = 0; r < KR; ++r) kring[r] = kread(kBase + r);
@@ -1193,7 +1204,8 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
   // of lane (lh, lsl) comes from rows r0 = 8 lh + (lsl >> 2) (+4, +16, +20)
   // of the tile: B(r0 + 4) = B(r0) + 273 and B(r0 + 16) = B(r0) + 1088
   // (r0 & 15 <= 11), so every read is one base register plus an immediate.
-  auto values = [&](const LDS_AS char* sv, const bf16x8 (&pw)[2]) {
+  // (hook(s) runs after value MFMA s: role 1 issues its tile loads there)
+  auto values = [&](const LDS_AS char* sv, const bf16x8 (&pw)[2], auto&& hook) {
     const int ln = fresh_lane(), lh = ln >> 5, lsl = ln & 15, ldh = (ln >> 4) & 1;
     const LDS_AS char* vb =
         sv + G::lat_base(8 * lh + (lsl >> 2)) + 16 * (2 * ldh + ((lsl & 3) >> 1)) + 8 * (lsl & 1);
@@ -1212,33 +1224,26 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
       const bf16x8 v = vring[s % VR];
       if (s + VR < 2 * kNB) vring[s % VR] = vread(s + VR);
       mfma_v(acc[s % kNB], v, pw[s / kNB]);
+      hook(s);
     }
   };
+  auto no_hook = [](int) {};
   // Role 0, phase B: softmax of tile i from this wave's partial scores S and
   // the partner's (from the slot); writes the bf16 weights to the slot.
-  auto softmax = [&](auto with_mask, floatx16& S, int i, bf16x8 (&pw)[2]) {
+  auto softmax = [&](auto with_mask, floatx16& S, const floatx4 (&sb)[4], int i, bf16x8 (&pw)[2]) {
     constexpr bool kMask = decltype(with_mask)::value;
     const int ln = fresh_lane();
-    const LDS_AS char* xs = smem + xs_off + 16 * ln;
     // token 16 (e >> 3) + 8 h + (e & 7) is visible iff 16 (e >> 3) + (e & 7)
     // < lim - (cb + 32 i) - 8 h: one bound, compared against immediates
     const int lim_h = lim - (cb + 32 * i) - 8 * (ln >> 5);
     float mx_a = neg_inf(), mx_b = neg_inf();
-    // (four scores at a time, each group its own scheduling region, so that
-    // few temporaries are live next to the accumulators)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const floatx4 sb = *(const LDS_AS floatx4*)(xs + 1024 * k);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int e = 4 * k + c;
-        float v = S[e] + sb[c];
-        if constexpr (kMask) v = 16 * (e >> 3) + (e & 7) < lim_h ? v : neg_inf();
-        S[e] = v;
-        if (e & 1) mx_b = __builtin_fmaxf(mx_b, v);
-        else mx_a = __builtin_fmaxf(mx_a, v);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int e = 0; e < 16; ++e) {
+      float v = S[e] + sb[e >> 2][e & 3];
+      if constexpr (kMask) v = 16 * (e >> 3) + (e & 7) < lim_h ? v : neg_inf();
+      S[e] = v;
+      if (e & 1) mx_b = __builtin_fmaxf(mx_b, v);
+      else mx_a = __builtin_fmaxf(mx_a, v);
     }
     // row maximum (both lane halves), times s = scale * log2 e > 0
     const float mx = half_swap_max(__builtin_fmaxf(mx_a, mx_b)) * scale_log2;
@@ -1249,16 +1254,16 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
     if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleMargin) != 0 && ln == 0)
       *(volatile LDS_AS uint32_t*)(smem + Lds::kRestart + 4 * (xs_off - Lds::kXchg) / kXchgSlot) = 1u;
     const float mu = m_ref == neg_inf() ? 0.0f : m_ref;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pw[e >> 3][e & 7] = (__bf16)fast_exp2(__builtin_fmaf(S[e], scale_log2, -mu));
+    // the normaliser sums the weights as the value product sees them (bf16),
+    // two at a time
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float la = 0.0f, lb = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const __bf16 w0 = (__bf16)fast_exp2(__builtin_fmaf(S[e], scale_log2, -mu));
-      const __bf16 w1 = (__bf16)fast_exp2(__builtin_fmaf(S[e + 1], scale_log2, -mu));
-      la += (float)w0;  // the normaliser sums the weights as the value product sees them
-      lb += (float)w1;
-      pw[e >> 3][e & 7] = w0;
-      pw[e >> 3][(e & 7) + 1] = w1;
-      if (e % 4 == 2) __builtin_amdgcn_sched_barrier(0);
+    for (int d = 0; d < 4; ++d) {
+      la = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pw[0][2 * d], pw[0][2 * d + 1]}, ones, la, false);
+      lb = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pw[1][2 * d], pw[1][2 * d + 1]}, ones, lb, false);
     }
     l_run += la + lb;
     // slot: weights [0, 2048) (the partner's partial scores there were read above)
@@ -1267,36 +1272,42 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
     *(LDS_AS bf16x8*)(xw + 1024) = pw[1];
   };
 
-  // ---- the tile loop.  Step i: phase A scores tile i (role 1 also issues the
-  // loads of tile i + 1, into the stage tile i - 2 left, and hands over its
-  // partial scores); phase B: role 0 runs the softmax of tile i and its half
-  // of tile i's value product while role 1 runs its half of tile i - 1's.
-  auto tile_g = [&](int i) {
-    return kv + kv_row_index<true>(p.page_table, p.MP, p.P, b, cb + 32 * i) * G::kRowBytes;
+  // ---- the tile loop, one workgroup barrier per step.  Step i: both waves
+  // score tile i.  Role 1 first issues the loads of tile i + 1 (into the stage
+  // tile i - 2 left); after its scores it hands over the partial scores, marks
+  // them ready and goes straight on to its half of tile i - 1's value product.
+  // Role 0 waits for the mark only, then runs the softmax of tile i and its
+  // half of tile i's value product.
+  // Role 1 reads the page of tile i + 2 during step i with a vector load (a
+  // scalar one would be waited for at the next LDS wait): it lands with the
+  // tile loads, which step i + 1 waits for anyway.
+  auto entry_of = [&](int i) { return kv_page_entry(p.page_table, p.MP, p.P, b, cb + 32 * i); };
+  auto tile_at = [&](int i, int page) { return kv + kv_row_of_page(page, p.P, cb + 32 * i) * G::kRowBytes; };
+  auto page_ahead = [&](int i) {  // entries of tiles past the last are never read
+    return i < ntiles ? entry_of(i)[fresh_lane() >> 6] : 0;  // (lane >> 6 == 0: one vector load)
   };
   for (;;) {  // once, unless a tile asks for a larger softmax reference
 #pragma unroll
     for (int db = 0; db < kNB; ++db) acc[db] = floatx16{};
     l_run = 0.0f;
-    if (ROLE == 1 && 0 < ntiles) pair_issue_bf16(tile_g(0), smem, pair, L - cb);
+    int pg_next = 0;  // role 1: page of tile i + 1 (in flight during step i - 1)
+    if (ROLE == 1 && 0 < ntiles) {
+      pair_issue_bf16<NP>(tile_at(0, uniform_load(entry_of(0))), smem, pair, L - cb);
+      pg_next = page_ahead(1);
+    }
     int so_cur = 0;  // stage offsets of tiles i and i - 1 (three stages, rotating)
     int so_prev = 2 * Lds::kCStage;
     bool restart = false;
     for (int i = 0; i <= ntiles; ++i) {
       if (ROLE == 1) wait_vmcnt<0>();  // tile i has landed
       __syncthreads();  // tile i is in its stage; every wave is done with step i - 1
-      {  // requests made by the softmax of tile i - 1 (no load is in flight here)
-        const uintx4 rq = *(const LDS_AS uintx4*)(smem + Lds::kRestart);
-        if (__builtin_amdgcn_readfirstlane((int)(rq[0] | rq[1] | rq[2] | rq[3])) != 0) {
-          restart = true;
-          break;
-        }
-      }
+      // requests made by the softmax of tile i - 1: read now, acted on after
+      // the scores, so that the read's latency is not in front of them
+      const uintx4 rq = *(const LDS_AS uintx4*)(smem + Lds::kRestart);
       const int so_next = so_cur == 2 * Lds::kCStage ? 0 : so_cur + Lds::kCStage;
       // (initialised here so that it is not carried from step to step)
       bf16x8 pw[2] = {bf16x8{}, bf16x8{}};  // role 0: the weights of tile i; role 1: those of tile i - 1
       if (ROLE == 1) {
-        if (i + 1 < ntiles) pair_issue_bf16(tile_g(i + 1), smem + so_next, pair, L - (cb + 32 * (i + 1)));
         if (i >= 1) {  // the weights of tile i - 1
           const int ln = fresh_lane();
           pw[0] = *(const LDS_AS bf16x8*)(smem + xs_off + 16 * ln);
@@ -1311,20 +1322,51 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
 #pragma unroll
           for (int k = 0; k < 4; ++k)
             *(LDS_AS floatx4*)(xw + 1024 * k) = floatx4{S[4 * k], S[4 * k + 1], S[4 * k + 2], S[4 * k + 3]};
+          // (LDS carries one wave's accesses in order: the mark lands after the scores)
+          *(volatile LDS_AS int*)(smem + Lds::kReady + 4 * pr_slot) = i + 1;
         }
       }
-      __syncthreads();  // the partial scores are in the slots
+      if (__builtin_amdgcn_readfirstlane((int)(rq[0] | rq[1] | rq[2] | rq[3])) != 0) {
+        restart = true;
+        break;
+      }
       if (ROLE == 0) {
         if (i == ntiles) break;
+        // the partner's partial scores of tile i, read together with its
+        // ready mark (one LDS round trip): LDS serves the partner's accesses
+        // in order, so when the mark read sees tile i the reads after it see
+        // the scores.  The partner is the older wave of the SIMD and usually
+        // done first; otherwise read again until the mark shows (it marks
+        // the scores right after its own score chain, so this wait ends).
+        floatx4 sb[4];
+        const volatile LDS_AS char* xs = smem + xs_off + 16 * fresh_lane();
+        for (;;) {
+          const int mark = *(const volatile LDS_AS int*)(smem + Lds::kReady + 4 * pr_slot);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) sb[k] = *(const volatile LDS_AS floatx4*)(xs + 1024 * k);
+          if (__builtin_amdgcn_readfirstlane(mark) > i) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
         const bool full = __builtin_amdgcn_ballot_w64(lim - (cb + 32 * i) < 32) == 0;
         if (__builtin_amdgcn_readfirstlane((int)full))
-          softmax(std::false_type{}, S, i, pw);
+          softmax(std::false_type{}, S, sb, i, pw);
         else
-          softmax(std::true_type{}, S, i, pw);
-        __builtin_amdgcn_sched_barrier(0);
-        values(smem + so_cur, pw);
+          softmax(std::true_type{}, S, sb, i, pw);
+        values(smem + so_cur, pw, no_hook);
       } else {
-        if (i >= 1) values(smem + so_prev, pw);
+        // the loads of tile i + 1 go out between the value MFMAs of tile
+        // i - 1: issuing them takes a while, and here no wave waits on it
+        const bool load_next = i + 1 < ntiles;
+        const char* tg = tile_at(load_next ? i + 1 : 0, __builtin_amdgcn_readfirstlane(pg_next));
+        const int vnext = L - (cb + 32 * (i + 1));
+        auto issue = [&](int k) {
+          if (load_next && k < kPairLoads<NP>) pair_issue_piece<NP>(tg, smem + so_next, pair, vnext, k);
+        };
+        if (i >= 1) values(smem + so_prev, pw, issue);
+        else issue(0);
+#pragma unroll
+        for (int k = i >= 1 ? 16 : 1; k < kPairLoads<NP>; ++k) issue(k);
+        pg_next = page_ahead(i + 2);
         if (i == ntiles) break;
       }
       so_prev = so_cur;
@@ -1334,8 +1376,9 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
     // rare path: every wave has read the requests before they are cleared;
     // the next run starts with the largest maximum seen as its reference
     mfma_drain();  // no value MFMA still writes the accumulators zeroed next
+    wait_vmcnt<0>();  // the loads role 1 issued this step have landed
     __syncthreads();
-    if (tid < 4) ((volatile LDS_AS uint32_t*)(smem + Lds::kRestart))[tid] = 0u;
+    if (tid < 8) ((volatile LDS_AS uint32_t*)(smem + Lds::kRestart))[tid] = 0u;
     m_ref = m_seen;
   }
 
@@ -1362,7 +1405,7 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
   // columns of the 32 rows at pitch kRowPitch, then each wave stores 16 whole
   // rows (role 0 rows 0..15, role 1 rows 16..31), 1 KB per store.
   LDS_AS char* wst = smem + pr * 32 * kRowPitch;
-  const int wrow0 = g * kPairRows + 32 * pr;  // unit row of staged row 0
+  const int wrow0 = g * kRows + 32 * pr;  // unit row of staged row 0
   auto stage_bf16 = [&]() {
 #pragma unroll
     for (int db = 0; db < kNB; ++db)
@@ -1422,17 +1465,21 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
   }
 }
 
-template <bool FP8>
-__global__ void __launch_bounds__(64 * kPairWaves, 1)
+template <int NP>
+__global__ void __launch_bounds__(128 * NP, 1)
 mla_split_pair(SplitParams p, int groups) {
-  using Lds = PairLds<FP8>;
-  constexpr int kWaves = kPairWaves;
+  using Lds = PairLds<NP>;
+  constexpr int kWaves = 2 * NP;
+  constexpr int kRows = 32 * NP;
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)(LDS_AS void*)smem_raw;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int pair = wave & 3, role = wave >> 2;
+  // Role 1 is the older wave of its SIMD: where both are ready to issue, the
+  // older one goes first, so its score chain (which role 0 waits for) finishes
+  // first.
+  const int pair = wave & (NP - 1), role = 1 - wave / NP;
 
   // Work of this workgroup: a list of segments, each a run of 32-token tiles
   // of one unit (request b, row group g).
@@ -1565,8 +1612,8 @@ mla_split_pair(SplitParams p, int groups) {
         sg.ce += p.prefix_len;
       }
       sg.final_out = p.write_final;
-      sg.drow = sg.final_out ? (int64_t)ub * M + (int64_t)ug * kPairRows
-                             : ((int64_t)ub * p.S + us) * M + (int64_t)ug * kPairRows;
+      sg.drow = sg.final_out ? (int64_t)ub * M + (int64_t)ug * kRows
+                             : ((int64_t)ub * p.S + us) * M + (int64_t)ug * kRows;
     } else {
       // Unit wu occupies positions [su, eu): kUnitStartCost positions, then
       // its tiles from ts = su + kUnitStartCost on.
@@ -1589,12 +1636,12 @@ mla_split_pair(SplitParams p, int groups) {
       sg.cb = 32 * (s0 - ts);
       sg.ce = 32 * (e - ts);
       if (sg.ce > L) sg.ce = L;
-      // Partial slots: [NB][2][kPairRows] rows.  Slot 0 holds the segment that
+      // Partial slots: [NB][2][kRows] rows.  Slot 0 holds the segment that
       // continues a unit begun in an earlier workgroup, slot 1 the one that
       // starts a unit and continues into later workgroups.
       sg.final_out = s0 == ts && e == eu;
-      sg.drow = sg.final_out ? (int64_t)b * M + (int64_t)sg.g * kPairRows
-                             : ((int64_t)wk * 2 + (s0 > ts ? 0 : 1)) * kPairRows;
+      sg.drow = sg.final_out ? (int64_t)b * M + (int64_t)sg.g * kRows
+                             : ((int64_t)wk * 2 + (s0 > ts ? 0 : 1)) * kRows;
       wx = e;
       ++wu;
       wsu = eu;
@@ -1603,31 +1650,32 @@ mla_split_pair(SplitParams p, int groups) {
     // the previous segment's waves are done with all of the LDS
     __syncthreads();
     if (role == 0)
-      pair_segment<FP8, 0>(p, smem, sg, pair, tid);
+      pair_segment<NP, 0>(p, smem, sg, pair, tid);
     else
-      pair_segment<FP8, 1>(p, smem, sg, pair, tid);
+      pair_segment<NP, 1>(p, smem, sg, pair, tid);
   }
 }
 
-template <bool FP8>
+template <int NP>
 hipError_t launch_pair(const SplitParams& p, hipStream_t stream) {
+  constexpr int kRows = 32 * NP;
   const int M = p.T * p.H;
-  const int groups = (M + kPairRows - 1) / kPairRows;
-  static_assert(kPairRows == kBalancedRows, "balanced units are one workgroup of rows");
+  const int groups = (M + kRows - 1) / kRows;
+  if (p.NB > 0 && kRows != kBalancedRows) return hipErrorInvalidValue;  // balanced units are 128 rows
   const int units = p.B * p.S;
   const int64_t blocks = p.NB > 0   ? (int64_t)p.NB
                          : p.Sp > 0 ? 8LL * ((p.S + 7) / 8) * p.B * groups  // cascade: chunk-major per XCD
                                     : 8LL * groups * ((units + 7) / 8);
-  const size_t lds = (size_t)PairLds<FP8>::kBytes;
+  const size_t lds = (size_t)PairLds<NP>::kBytes;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
-    attr_err = hipFuncSetAttribute((const void*)mla_split_pair<FP8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    attr_err = hipFuncSetAttribute((const void*)mla_split_pair<NP>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)lds);
   });
   if (attr_err != hipSuccess) return attr_err;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((mla_split_pair<FP8>), dim3((unsigned)blocks), dim3(64 * kPairWaves), lds, stream, p,
+  hipLaunchKernelGGL((mla_split_pair<NP>), dim3((unsigned)blocks), dim3(128 * NP), lds, stream, p,
                      groups);
   return hipGetLastError();
 }
@@ -2569,11 +2617,39 @@ Kernel pick_kernel(const SplitParams& p) {
   return p.kv_dtype == kFP8 ? Kernel::kMfmaFp8 : Kernel::kMfmaBf16;
 }
 
+// Compute units of the current device (cached per device).
+int current_device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// bf16 KV: the wave-pair kernel, 128-row workgroups unless a uniform plan
+// would then leave compute units idle and 64-row ones give more workgroups.
+// (MLA_MFMA_KERNEL=four at load time selects the four-wave kernel instead.)
+hipError_t launch_bf16_mfma(const SplitParams& p, hipStream_t stream) {
+  static const bool four = [] {
+    const char* sel = getenv("MLA_MFMA_KERNEL");
+    return sel && sel[0] == 'f';
+  }();
+  if (four) return launch_mfma<false, 4, 4>(p, stream);
+  if (p.NB == 0) {
+    const int64_t M = (int64_t)p.T * p.H;
+    const int64_t wg128 = (int64_t)p.B * p.S * ((M + 127) / 128);
+    if (M > 64 && wg128 < current_device_cus()) return launch_pair<2>(p, stream);
+  }
+  return launch_pair<4>(p, stream);
+}
+
 hipError_t launch_split(const SplitParams& p, hipStream_t stream) {
-  const char* sel = getenv("MLA_MFMA_KERNEL");
-  const bool four = sel && sel[0] == 'f';
   switch (pick_kernel(p)) {
-    case Kernel::kMfmaBf16: return four ? launch_mfma<false, 4, 4>(p, stream) : launch_pair<false>(p, stream);
+    case Kernel::kMfmaBf16: return launch_bf16_mfma(p, stream);
     case Kernel::kMfmaFp8: return launch_mfma<true, 4, 8>(p, stream);
     default: break;
   }
