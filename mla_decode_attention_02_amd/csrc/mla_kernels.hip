@@ -20,7 +20,6 @@
 #include <stdint.h>
 #include <stdlib.h>
 
-#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -1002,9 +1001,8 @@ mla_split_mfma(SplitParams p, int groups) {
 
 // --------------------------------------------- MFMA split kernel, wave pairs
 // One workgroup = NP pairs of wavefronts (NP = 4: 8 waves, 128 query rows,
-// the unit of the balanced work list; NP = 2: 4 waves, 64 rows, for uniform
-// plans that would otherwise leave compute units idle) over rows of one
-// request b (row r = t * H + h, the query-token fold).  Pair p (waves p and
+// the unit of the balanced work list, the one launched; NP = 2: 4 waves, 64
+// rows) over rows of one request b (row r = t * H + h, the query-token fold).  Pair p (waves p and
 // p + NP) owns rows 32p .. 32p + 31 of the workgroup and splits both
 // contractions in halves: role 0 (wave p + NP) forms the partial scores over
 // dims [0, 288) of the 576-deep dot and owns output columns [0, 256); role 1
@@ -2617,33 +2615,17 @@ Kernel pick_kernel(const SplitParams& p) {
   return p.kv_dtype == kFP8 ? Kernel::kMfmaFp8 : Kernel::kMfmaBf16;
 }
 
-// Compute units of the current device (cached per device).
-int current_device_cus() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = cached[dev].load(std::memory_order_relaxed);
-  if (v <= 0) {
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cached[dev].store(v, std::memory_order_relaxed);
-  }
-  return v;
-}
-
-// bf16 KV: the wave-pair kernel, 128-row workgroups unless a uniform plan
-// would then leave compute units idle and 64-row ones give more workgroups.
-// (MLA_MFMA_KERNEL=four at load time selects the four-wave kernel instead.)
+// bf16 KV: the wave-pair kernel with 128-row workgroups.  (Workgroups of
+// two pairs would fill the chip where a uniform plan has fewer units than
+// compute units, but one wave per SIMD runs them slower than half the chip
+// runs the four-pair ones.)  MLA_MFMA_KERNEL=four at load time selects the
+// four-wave kernel instead.
 hipError_t launch_bf16_mfma(const SplitParams& p, hipStream_t stream) {
   static const bool four = [] {
     const char* sel = getenv("MLA_MFMA_KERNEL");
     return sel && sel[0] == 'f';
   }();
   if (four) return launch_mfma<false, 4, 4>(p, stream);
-  if (p.NB == 0) {
-    const int64_t M = (int64_t)p.T * p.H;
-    const int64_t wg128 = (int64_t)p.B * p.S * ((M + 127) / 128);
-    if (M > 64 && wg128 < current_device_cus()) return launch_pair<2>(p, stream);
-  }
   return launch_pair<4>(p, stream);
 }
 
