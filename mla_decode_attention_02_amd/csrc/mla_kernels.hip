@@ -1180,7 +1180,7 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
       return kk < 32 ? *(const LDS_AS bf16x8*)(kb + 32 * kk)
                      : *(const LDS_AS bf16x8*)(rb + 16 * ((2 * (kk - 32) + h) ^ swr));
     };
-    constexpr int KR = ROLE ? 3 : 2;  // role 1 has the registers for a deeper ring
+    constexpr int KR = 4;  // key fragments in flight
     bf16x8 kring[KR], qk_reg[kQLds];
 #pragma unroll
     for (int r = 0; r < KR; ++r) kring[r] = kread(kBase + r);
@@ -1188,7 +1188,7 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
     for (int s = 0; s < 18; ++s) {
       const bf16x8 a = kring[s % KR];
       if (s + KR < 18) kring[s % KR] = kread(kBase + s + KR);
-      constexpr int kAhead = 4;  // kept fragments are read this many steps before use
+      constexpr int kAhead = 2;  // kept fragments are read this many steps before use
       if (s + kAhead >= kQReg && s + kAhead < 18) qk_reg[s + kAhead - kQReg] = *(const LDS_AS bf16x8*)(qk + 1024 * (s + kAhead - kQReg));
       const bf16x8 q = s < kQReg ? qf[s < kQReg ? s : 0] : qk_reg[s < kQReg ? 0 : s - kQReg];
       if (s == 0) mfma_v0(S, a, q);
