@@ -152,7 +152,8 @@ def pmc_summary(pmc_dir, workload, num_splits, calib_mib, out_path=None):
     run = (f"python -u $REPO/bench.py --steps 5 --warmup 2 --no-cpu --no-sub --no-probe --workload {workload}"
            f"{'' if num_splits < 0 else f' --num-splits {num_splits}'} --calib-copy-mib {calib_mib}")
     lines = [
-        f"# HBM traffic of mla_split_mfma, workload {workload}",
+        f"# HBM traffic of {split_kernel_name(next(x for x in synth.WORKLOADS if x.name == workload))}, "
+        f"workload {workload}",
         "",
         "Commands (the two profiled runs from /tmp with TMPDIR=/tmp; REPO = repository root):",
         "",
@@ -179,11 +180,21 @@ def pmc_summary(pmc_dir, workload, num_splits, calib_mib, out_path=None):
     print("\n".join(lines))
 
 
+def split_kernel_name(w):
+    """The split kernel the library runs for workload w: the wave-pair MFMA
+    kernel for bf16 KV, the four-wave one for E4M3 KV, the VALU one for other
+    widths."""
+    if w.d_latent != 512 or w.d_rope != 64 or w.q_dtype != "bf16":
+        return "mla_split_generic"
+    return {"bf16": "mla_split_pair", "fp8": "mla_split_mfma"}.get(w.kv_dtype, "mla_split_generic")
+
+
 def traffic_path(workload, plan_key):
     """Where the HBM-traffic summary of the split kernel for this workload and
     launch configuration (plan key: "balanced", or "s<S>" for S uniform
     chunks per request) lives under profiles/."""
-    return os.path.join(PROFILES, f"mla_split_mfma__{workload}__{plan_key}__traffic.md")
+    w = next(x for x in synth.WORKLOADS if x.name == workload)
+    return os.path.join(PROFILES, f"{split_kernel_name(w)}__{workload}__{plan_key}__traffic.md")
 
 
 def recorded_traffic(workload, plan_key):
@@ -574,7 +585,7 @@ def measure_decode(mla, w, inp, args, S_req, cascade=False):
         roof["traffic"] = None
     else:
         roof["traffic"] = recorded_traffic(w.name, pkey)
-    roof["kernel"] = "mla_split_mfma" if w.d_latent == 512 else "mla_split_generic"
+    roof["kernel"] = split_kernel_name(w)
     roof["per_launch_algorithmic"] = alg_split["bytes"] if bound == "hbm" else alg_split["flops"]
     roof["kernel_avg_ms"] = round(split_avg, 5)
     roof["path_roofline_ms"] = round(max(t_hbm, t_mfma) * 1e3, 5)
