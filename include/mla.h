@@ -24,7 +24,10 @@
  * Blackwell kernel: a split stage writes fp32 partial results per chunk of
  * the sequence into a workspace, and a reduction stage merges them by
  * log-sum-exp rescaling and casts to the output type.  mla_decode() runs both;
- * mla_decode_split() and mla_combine() expose them separately.
+ * mla_decode_split() and mla_combine() expose them separately.  (The uniform
+ * plan's partials are fp32 as described; the balanced work list, mla_decode's
+ * default where it would split, keeps its few per-workgroup partial rows in
+ * bf16 with fp32 log-sum-exp: see mla_decode_split_balanced.)
  *
  * Conventions for every entry point:
  *   - All array arguments are DEVICE pointers unless marked "host"; the
@@ -106,7 +109,9 @@ typedef struct {
 
 /*
  * Number of sequence chunks S of the uniform split plan for this problem
- * (>= 1), written to *num_splits.  Chunk k of request b covers tokens
+ * (>= 1), written to *num_splits: the split-KV plan of the code-audit
+ * article's MLA entries (the split stage covers one chunk of the sequence
+ * per workgroup and the reduction stage merges the chunks).  Chunk k of request b covers tokens
  * [k C_b, min((k+1) C_b, L_b)) with C_b = P * ceil(ceil(L_b / S) / P), so
  * chunks are page aligned and empty chunks are allowed.  mla_decode() runs
  * this plan when num_splits is forced, when S == 1, or when the shape takes
@@ -122,7 +127,9 @@ typedef struct {
 int mla_num_splits(const mla_problem* problem, int32_t* num_splits);
 
 /* Bytes of device workspace mla_decode() needs on the current device (0 when
- * it never splits), to *bytes.  The balanced work list's share depends on the
+ * it never splits), to *bytes: the buffer the split stage writes its partial
+ * results (and their log-sum-exp) into for the reduction stage, the
+ * workspace of the code-audit article's MLA entries.  The balanced work list's share depends on the
  * device's compute-unit count, so size the workspace on the device that runs
  * the call. */
 int mla_workspace_size(const mla_problem* problem, size_t* bytes);
@@ -345,7 +352,6 @@ int mla_project(int32_t rows, int32_t heads, int32_t in_dim, int32_t out_dim, co
                 const void* w, int32_t out_dtype, void* out, hipStream_t stream);
 
 /*
- * Test hook for the page-table loader/*
  * Test hook for the page-table loader: copies, bit for bit, the stored rows
  * of logical token tok[i] of request req[i] (i < n) into out [n, Dc+Dr]
  * (kv_dtype elements), resolving pages with the same device address routine

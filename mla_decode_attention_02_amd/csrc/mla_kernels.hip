@@ -53,9 +53,10 @@ __device__ __forceinline__ T uniform_load(const T* p) {
 // ------------------------------------------------------------------ loader
 // Physical row of logical token j of request b: the block table maps the
 // request's logical page j / P to a physical page, and j mod P is the slot in
-// it ("推理优化" tag page, PagedAttention article).  The decode kernels and the
-// gather hook resolve rows through this routine; kUniform reads the table
-// entry through the scalar cache (b and j the same in every lane).
+// it ("推理优化" tag page, PagedAttention article).  The decode kernels, the
+// append kernel and the gather hook resolve rows through this routine;
+// kUniform reads the table entry through the scalar cache (b and j the same
+// in every lane).
 // (kv_page_entry and kv_row_of_page are its two halves, for callers that
 // read the entry ahead of its use.)
 __device__ __forceinline__ const int32_t* kv_page_entry(const int32_t* __restrict__ page_table, int MP,
@@ -2170,7 +2171,7 @@ mla_append_kernel(int B, int T, int D, int P, int MP, int src_dtype, int kv_dtyp
   if (idx >= (int64_t)B * T) return;
   const int b = (int)(idx / T), t = (int)(idx - (int64_t)b * T);
   const int pos = pos0[b] + t;
-  const int64_t row = (int64_t)page_table[(int64_t)b * MP + pos / P] * P + pos % P;
+  const int64_t row = kv_row_index(page_table, MP, P, b, pos);  // the write side of the same mapping
   auto value = [&](int d) -> float {
     return src_dtype == kF32 ? ((const float*)src)[idx * D + d]
                              : bf16_bits_to_float(((const uint16_t*)src)[idx * D + d]);
