@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from helpers import assert_close, metrics, run_decode, small, to_device, tolerance
+from helpers import TOL, assert_close, metrics, run_decode, small, to_device, tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -432,3 +432,23 @@ def test_full_size_workload_every_request(mla, index, num_splits):
     fin = np.isfinite(rl)
     assert np.array_equal(np.isfinite(lse), fin)
     assert np.abs(lse[fin] - rl[fin]).max() <= 1e-3 * max(1.0, np.abs(rl[fin]).max())
+
+
+def test_balanced_bf16_partials_error_against_fp32_partials(mla):
+    """The balanced work list keeps its partial rows in bf16 (fp32 lse); the
+    uniform plan keeps fp32 partials, as the split-KV description has them.
+    At the DeepSeek shape, with fp32 outputs so that only the partials'
+    precision differs, both are compared with the oracle: the bf16 slots must
+    stay within the bf16 bar, and the two errors are printed side by side."""
+    w = synth.workload(1)
+    inp = synth.make_inputs(w)
+    dev = to_device(inp)
+    ob, lb = run_decode(mla, inp, dev=dev, num_splits=0, out_dtype="f32")  # balanced, bf16 slots
+    ou, lu = run_decode(mla, inp, dev=dev, num_splits=4, out_dtype="f32")  # uniform, fp32 partials
+    ro, rl = oracle.attend(inp)
+    eb = metrics(ob, ro)
+    eu = metrics(ou, ro)
+    print(f"{w.name} fp32 out: balanced (bf16 partial rows) max_abs {eb[0]:.3e} mean_rel {eb[1]:.3e}; "
+          f"uniform S=4 (fp32 partials) max_abs {eu[0]:.3e} mean_rel {eu[1]:.3e}", flush=True)
+    assert eb[0] <= TOL["bf16"][0] and eb[1] <= TOL["bf16"][1]
+    assert eu[0] <= TOL["bf16"][0] and eu[1] <= TOL["bf16"][1]
