@@ -2619,14 +2619,11 @@ Kernel pick_kernel(const SplitParams& p) {
 // bf16 KV: the wave-pair kernel with 128-row workgroups.  (Workgroups of
 // two pairs would fill the chip where a uniform plan has fewer units than
 // compute units, but one wave per SIMD runs them slower than half the chip
-// runs the four-pair ones.)  MLA_MFMA_KERNEL=four at load time selects the
-// four-wave kernel instead.
+// runs the four-pair ones.)  The environment variable MLA_MFMA_KERNEL=four
+// (read at each launch) selects the four-wave kernel instead.
 hipError_t launch_bf16_mfma(const SplitParams& p, hipStream_t stream) {
-  static const bool four = [] {
-    const char* sel = getenv("MLA_MFMA_KERNEL");
-    return sel && sel[0] == 'f';
-  }();
-  if (four) return launch_mfma<false, 4, 4>(p, stream);
+  const char* sel = getenv("MLA_MFMA_KERNEL");
+  if (sel && sel[0] == 'f') return launch_mfma<false, 4, 4>(p, stream);
   return launch_pair<4>(p, stream);
 }
 

@@ -452,3 +452,12 @@ def test_balanced_bf16_partials_error_against_fp32_partials(mla):
           f"uniform S=4 (fp32 partials) max_abs {eu[0]:.3e} mean_rel {eu[1]:.3e}", flush=True)
     assert eb[0] <= TOL["bf16"][0] and eb[1] <= TOL["bf16"][1]
     assert eu[0] <= TOL["bf16"][0] and eu[1] <= TOL["bf16"][1]
+
+
+def test_four_wave_kernel_on_bf16(mla, monkeypatch):
+    """MLA_MFMA_KERNEL=four runs bf16 KV on the four-wave kernel (the one E4M3
+    KV always takes): uniform and balanced plans agree with the oracle."""
+    monkeypatch.setenv("MLA_MFMA_KERNEL", "four")
+    check_against_oracle(mla, synth.make_inputs(DS_SMALL), 2, "four-wave S=2")
+    w = BALANCED_CASES["mixed"]
+    check_against_oracle(mla, synth.make_inputs(w), 0, "four-wave balanced")
