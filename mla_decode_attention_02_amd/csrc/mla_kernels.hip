@@ -2107,6 +2107,165 @@ mla_combine_balanced4_kernel(int B, int M, int Dc, int NB, const int32_t* __rest
   }
 }
 
+// Balanced-plan merge for units that span many workgroups (a few long
+// requests): the partials of a row-quad are spread over WV = 2, 4 or 8
+// wavefronts (M a multiple of 4, Dc a multiple of 8 and at most 512).  Every
+// wavefront reads the four rows' lse of the first 64 partials (lane j holds
+// partial j) and, in the same round trip, the rows of its own share of the
+// partials (j = wave, wave + WV, ...; eight partials in flight), so a
+// row-quad costs two dependent memory round trips (tile prefix, then lse
+// plus rows) when it has at most 8 WV partials; the wavefronts' sums are
+// added through LDS.  Same weights as the kernels above (normalised once per
+// row); the partials are summed in a different order.
+constexpr int kWideSlotsInFlight = 8;
+
+template <int WV>
+struct WideMerge {
+  static_assert(WV == 2 || WV == 4 || WV == 8, "two, four or eight wavefronts per row-quad");
+  static constexpr int kQuads = WV >= 4 ? 1 : 4 / WV;  // row-quads per workgroup
+  static constexpr int kThreads = kQuads * WV * 64;
+  static constexpr int kRed = kQuads * WV * kMergeRows * 512;  // floats of LDS
+};
+
+template <int WV>
+__global__ void __launch_bounds__(WideMerge<WV>::kThreads)
+mla_combine_balanced_wide_kernel(int B, int M, int Dc, int NB, const int32_t* __restrict__ prefix,
+                                 const __bf16* __restrict__ po, const float* __restrict__ pl, int out_dtype,
+                                 void* out, float* lse) {
+  using G = WideMerge<WV>;
+  __shared__ float red[G::kRed];  // [quad][wavefront][row][column]
+  const int lane = threadIdx.x & 63;
+  const int quad = (threadIdx.x >> 6) / WV, wave = (threadIdx.x >> 6) % WV;
+  const int64_t idx0 = ((int64_t)blockIdx.x * G::kQuads + quad) * kMergeRows;  // the quad's first row
+  const int d = 8 * lane;
+  const bool ok = d < Dc;
+  bool merged = false;  // this quad's rows are written by this kernel from partials
+  float mx[kMergeRows], wsum[kMergeRows];
+  float acc[kMergeRows][8];
+#pragma unroll
+  for (int rr = 0; rr < kMergeRows; ++rr) {
+    mx[rr] = neg_inf();
+    wsum[rr] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[rr][e] = 0.0f;
+  }
+  if (idx0 < (int64_t)B * M) {
+    const int b = (int)(idx0 / M), r0 = (int)(idx0 - (int64_t)b * M);
+    const int groups = (M + kBalancedRows - 1) / kBalancedRows;
+    const int g = r0 / kBalancedRows, lr0 = r0 - g * kBalancedRows;
+    const int u = b * groups + g;
+    const int64_t W = prefix[B * groups];
+    const int64_t su = prefix[u], eu = prefix[u + 1];
+    const int64_t nb = W < NB ? W : NB;
+    const int k1 = su == eu ? 0 : (int)(((su + kUnitStartCost + 1) * nb + W - 1) / W - 1);
+    const int k2 = su == eu ? 0 : (int)((eu * nb + W - 1) / W - 1);
+    if (su == eu) {  // no visible token: out = 0, lse = -inf (wavefront 0 of the quad)
+      if (wave == 0) {
+        for (int rr = 0; rr < kMergeRows; ++rr) {
+          const int64_t ob = (idx0 + rr) * Dc;
+          for (int c = lane; c < Dc; c += 64) {
+            if (out_dtype == kBF16) ((__bf16*)out)[ob + c] = (__bf16)0.0f;
+            else ((float*)out)[ob + c] = 0.0f;
+          }
+        }
+        if (lse && lane < kMergeRows) lse[idx0 + lane] = neg_inf();
+      }
+    } else if (k1 != k2) {  // k1 == k2: written by the split kernel
+      merged = true;
+      const int ns = k2 - k1 + 1;
+      auto slot_row = [&](int j) -> int64_t {  // row lr0 of partial j's slot
+        const int64_t slot = j == 0 ? 2LL * k1 + 1 : 2LL * (k1 + j);
+        return slot * kBalancedRows + lr0;
+      };
+      auto weight = [](float v, float m) { return v == neg_inf() ? 0.0f : fast_exp2((v - m) * kLog2e); };
+      float l0[kMergeRows];  // lse of partial `lane` (first 64 partials)
+      {
+        const int64_t row = slot_row(lane < ns ? lane : 0);
+#pragma unroll
+        for (int rr = 0; rr < kMergeRows; ++rr) l0[rr] = lane < ns ? pl[row + rr] : neg_inf();
+      }
+      bf16x8 raw[kWideSlotsInFlight][kMergeRows];
+      auto load_batch = [&](int jb) {
+#pragma unroll
+        for (int q = 0; q < kWideSlotsInFlight; ++q) {
+          const int j = jb + WV * q;
+          const bool live = ok && j < ns;
+          const int64_t row = slot_row(j < ns ? j : 0);
+#pragma unroll
+          for (int rr = 0; rr < kMergeRows; ++rr)
+            raw[q][rr] = live ? *(const bf16x8*)(po + (row + rr) * Dc + d) : bf16x8{};
+        }
+      };
+      load_batch(wave);  // in flight with the lse loads
+      float inv[kMergeRows], wl[kMergeRows];
+#pragma unroll
+      for (int rr = 0; rr < kMergeRows; ++rr) {
+        float m = l0[rr];
+        for (int j = lane + 64; j < ns; j += 64) m = fmaxf(m, pl[slot_row(j) + rr]);
+        mx[rr] = wave_max(m);
+        float sm = weight(l0[rr], mx[rr]);
+        for (int j = lane + 64; j < ns; j += 64) sm += weight(pl[slot_row(j) + rr], mx[rr]);
+        wsum[rr] = wave_sum(sm);
+        inv[rr] = wsum[rr] > 0.0f ? 1.0f / wsum[rr] : 0.0f;
+        wl[rr] = weight(l0[rr], mx[rr]) * inv[rr];  // weight of partial `lane`
+      }
+      for (int jb = wave;;) {
+#pragma unroll
+        for (int q = 0; q < kWideSlotsInFlight; ++q) {
+          const int j = jb + WV * q;
+          if (j >= ns) break;  // uniform over the wavefront
+#pragma unroll
+          for (int rr = 0; rr < kMergeRows; ++rr) {
+            const float w = j < 64 ? __shfl(wl[rr], j, 64) : weight(pl[slot_row(j) + rr], mx[rr]) * inv[rr];
+            if (w != 0.0f) {  // a zero-weight partial's row may hold anything
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[rr][e] = __builtin_fmaf(w, (float)raw[q][rr][e], acc[rr][e]);
+            }
+          }
+        }
+        jb += WV * kWideSlotsInFlight;
+        if (jb >= ns) break;
+        load_batch(jb);
+      }
+    }
+  }
+  {
+    float* qred = red + quad * (WV * kMergeRows * 512);
+    if (merged && ok) {
+#pragma unroll
+      for (int rr = 0; rr < kMergeRows; ++rr)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qred[(wave * kMergeRows + rr) * 512 + d + e] = acc[rr][e];
+    }
+    __syncthreads();  // reached by every thread: no early return above
+    if (merged) {
+      // the quad's threads finish 4 rows x 128 column-quads
+      for (int it = wave * 64 + lane; it < kMergeRows * 128; it += WV * 64) {
+        const int rr = it >> 7, c = 4 * (it & 127);
+        if (c >= Dc) continue;
+        float a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float s = 0.0f;
+#pragma unroll
+          for (int v = 0; v < WV; ++v) s += qred[(v * kMergeRows + rr) * 512 + c + e];
+          a[e] = s;
+        }
+        const int64_t ob = (idx0 + rr) * Dc + c;
+        if (out_dtype == kBF16) {
+          *(bf16x4*)((__bf16*)out + ob) = bf16x4{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]};
+        } else {
+          *(floatx4*)((float*)out + ob) = floatx4{a[0], a[1], a[2], a[3]};
+        }
+      }
+    }
+  }
+  if (merged && lse && wave == 0 && lane == 0) {
+#pragma unroll
+    for (int rr = 0; rr < kMergeRows; ++rr) lse[idx0 + rr] = wsum[rr] > 0.0f ? mx[rr] + __logf(wsum[rr]) : neg_inf();
+  }
+}
+
 // ------------------------------------------------------------- KV append
 // Paged KV append with packing: token t of request b is stored at logical
 // position pos[b] + t, i.e. page page_table[b][pos / P], slot pos mod P
@@ -2657,6 +2816,27 @@ hipError_t launch_combine_balanced(int32_t B, int32_t M, int32_t Dc, int32_t NB,
                                    hipStream_t stream) {
   const int64_t n = (int64_t)B * M;
   if (n == 0) return hipSuccess;
+  if (M % kMergeRows == 0 && Dc % 8 == 0 && Dc <= 512) {
+    // wavefronts per row-quad from the average number of partials per unit
+    // (measured: the single-wavefront merge is faster up to about 8)
+    const int64_t units = (int64_t)B * ((M + kBalancedRows - 1) / kBalancedRows);
+    const int64_t per_unit = NB / units + 1;
+    const int64_t quads = n / kMergeRows;
+    auto grid = [&](int q) { return dim3((unsigned)((quads + q - 1) / q)); };
+    if (per_unit > 32)
+      hipLaunchKernelGGL(mla_combine_balanced_wide_kernel<8>, grid(WideMerge<8>::kQuads), dim3(WideMerge<8>::kThreads),
+                         0, stream, B, M, Dc, NB, tile_prefix, (const __bf16*)part_o, part_lse, out_dtype, out, lse);
+    else if (per_unit > 16)
+      hipLaunchKernelGGL(mla_combine_balanced_wide_kernel<4>, grid(WideMerge<4>::kQuads), dim3(WideMerge<4>::kThreads),
+                         0, stream, B, M, Dc, NB, tile_prefix, (const __bf16*)part_o, part_lse, out_dtype, out, lse);
+    else if (per_unit > 8)
+      hipLaunchKernelGGL(mla_combine_balanced_wide_kernel<2>, grid(WideMerge<2>::kQuads), dim3(WideMerge<2>::kThreads),
+                         0, stream, B, M, Dc, NB, tile_prefix, (const __bf16*)part_o, part_lse, out_dtype, out, lse);
+    else  // a few partials per unit: one wavefront per row-quad
+      hipLaunchKernelGGL(mla_combine_balanced4_kernel, dim3((unsigned)((quads + 3) / 4)), dim3(256), 0, stream, B, M,
+                         Dc, NB, tile_prefix, (const __bf16*)part_o, part_lse, out_dtype, out, lse);
+    return hipGetLastError();
+  }
   if (M % kMergeRows == 0 && Dc % 8 == 0) {
     const int64_t waves = n / kMergeRows;
     hipLaunchKernelGGL(mla_combine_balanced4_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, B, M,

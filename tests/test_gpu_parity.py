@@ -131,6 +131,12 @@ BALANCED_CASES = {
     # wavefront), and 132 rows: a second row group of four rows
     "six_heads": small(1, batch=3, heads=6, seq_lens=("fixed", (3000, 17, 900)), decoys=2, index=45),
     "heads_132": small(1, batch=2, heads=132, seq_lens=("fixed", (2500, 700)), decoys=2, index=46),
+    # units of about 22 and about 11 partials on 256 workgroups: the merge
+    # spreads a row-quad's partials over four and over two wavefronts
+    "twelve_requests": small(1, batch=12, seq_lens=("fixed", (3000, 50, 1200, 0, 800, 2500, 64, 1, 4000, 300,
+                                                               1500, 2000)), decoys=2, index=47),
+    "twenty_four_requests": small(1, batch=24, seq_lens=("fixed", (900, 20, 1500, 0, 640, 1100, 64, 3, 2000, 150,
+                                                                   700, 1000) * 2), decoys=2, index=48),
 }
 
 
