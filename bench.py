@@ -182,11 +182,11 @@ def pmc_summary(pmc_dir, workload, num_splits, calib_mib, out_path=None):
 
 def split_kernel_name(w):
     """The split kernel the library runs for workload w: the wave-pair MFMA
-    kernel for bf16 KV, the four-wave one for E4M3 KV, the VALU one for other
-    widths."""
-    if w.d_latent != 512 or w.d_rope != 64 or w.q_dtype != "bf16":
+    kernel for bf16 and E4M3 KV (the four-wave one under MLA_MFMA_KERNEL=four),
+    the VALU one for other widths."""
+    if w.d_latent != 512 or w.d_rope != 64 or w.q_dtype != "bf16" or w.kv_dtype not in ("bf16", "fp8"):
         return "mla_split_generic"
-    return {"bf16": "mla_split_pair", "fp8": "mla_split_mfma"}.get(w.kv_dtype, "mla_split_generic")
+    return "mla_split_mfma" if os.environ.get("MLA_MFMA_KERNEL", "").startswith("f") else "mla_split_pair"
 
 
 def traffic_path(workload, plan_key):

@@ -53,9 +53,9 @@
  *     seq_len is outside [0, max_pages_per_seq * page_size].  Never use it
  *     under graph capture.
  *   - Kernel selection for comparisons (read at each call): MLA_KERNEL=generic
- *     runs every decode on the VALU kernel; MLA_MFMA_KERNEL=four runs bf16 KV
- *     on the four-wave MFMA kernel (the one E4M3 KV takes) instead of the
- *     wave-pair kernel.  Results agree up to rounding.
+ *     runs every decode on the VALU kernel; MLA_MFMA_KERNEL=four runs bf16
+ *     and E4M3 KV on the four-wave MFMA kernel instead of the wave-pair
+ *     kernel.  Results agree up to rounding.
  */
 #ifndef MLA_DECODE_H_
 #define MLA_DECODE_H_

@@ -1022,9 +1022,14 @@ mla_split_mfma(SplitParams p, int groups) {
 //   role 0  scores tile i, waits for the mark, adds the partial, runs the
 //           softmax (lazy reference, see kRescaleMargin), writes the bf16
 //           weights to the slot and runs its half of tile i's value product.
-// LDS: three bf16 tile stages, one 4 KB exchange slot per pair (partial
-// scores, then weights, at the end 1 / normaliser), the kept query
-// fragments, one restart word and one ready mark per pair.
+// LDS: three tile stages, one 4 KB exchange slot per pair (partial scores,
+// then weights, at the end 1 / normaliser), the kept query fragments, one
+// restart word and one ready mark per pair.
+// E4M3 KV (the quantisation article's FP8 table; code-audit article, FP8 KV
+// cache entry): the stages hold codes and per-token scales; each wave
+// converts to bf16 only the key half it scores and the value columns it
+// owns, at the operand read; role 0 multiplies the summed scores and the
+// weights by the token scales (the normaliser takes the weights alone).
 constexpr int kXchgSlot = 4096;
 constexpr int kRowPitch = 1024 + 16;             // staged query / output rows
 constexpr int kQRegion = 32 * kRowPitch + 32 * 128;
@@ -1037,10 +1042,11 @@ constexpr int kQLds = 3, kQReg = 18 - kQLds;
 // a larger reference; below it every weight and partial sum stays under 2^60.
 constexpr float kRescaleMargin = 60.0f;
 
-template <int NP>
+template <int NP, bool FP8 = false>
 struct PairLds {
   static_assert(NP == 2 || NP == 4, "two or four pairs per workgroup");
-  static constexpr int kCStage = Tile<false>::kStage;
+  static_assert(!FP8 || NP == 4, "E4M3 tiles: four pairs");
+  static constexpr int kCStage = Tile<FP8>::kStage;
   static constexpr int kXchg = 3 * kCStage;             // exchange slots, one per pair
   static constexpr int kQKeep = kXchg + NP * kXchgSlot;  // per wave: the query fragments kept in LDS
   static constexpr int kRestart = kQKeep + 2 * NP * kQLds * 1024;  // one restart word per pair (4 words)
@@ -1059,41 +1065,66 @@ struct PairSegment {
   int64_t drow;
 };
 
-// Direct HBM -> LDS loads of one bf16 tile by role-1 wave bw (0 .. NP - 1),
-// kPairLoads<NP> of them: load k < 32 / NP is latent row bw + NP k, the rest
-// the rope of the 8-row groups c = bw + NP j (rows 8c .. 8c + 7).  Rows at or
-// past `valid` (slots past the request's end, which may hold anything) are
-// loaded from row valid - 1 instead: their scores are masked and their
-// weights are exactly 0, so a finite duplicate row contributes nothing.
-template <int NP>
-constexpr int kPairLoads = 32 / NP + 4 / NP;
-template <int NP>
-__device__ __forceinline__ void pair_issue_piece(const char* tile_g, LDS_AS char* st, int bw, int valid, int k) {
-  using G = Tile<false>;
+// Direct HBM -> LDS loads of one tile by role-1 wave bw (0 .. NP - 1),
+// kPairLoads<NP, FP8> of them.  bf16: load k < 32 / NP is latent row
+// bw + NP k, the rest the rope of the 8-row groups c = bw + NP j (rows
+// 8c .. 8c + 7).  E4M3 (NP = 4): load k < 4 is latent rows pr = bw + 4k and
+// pr + 16 (one 1056-byte block), the last one the rope of rows 16 bw ..
+// 16 bw + 15 (bw < 2) or the tile's 32 token scales (bw >= 2; both such
+// waves write the same bytes).  Rows at or past `valid` (slots past the
+// request's end, which may hold anything) are loaded from row valid - 1
+// instead: their scores are masked and their weights are exactly 0, so a
+// finite duplicate row contributes nothing.  (Scales past the end are not
+// replaced; the softmax zeroes those tokens' scales.)
+template <int NP, bool FP8>
+constexpr int kPairLoads = FP8 ? 16 / NP + 1 : 32 / NP + 4 / NP;
+template <int NP, bool FP8>
+__device__ __forceinline__ void pair_issue_piece(const char* tile_g, const float* scale_g, LDS_AS char* st, int bw,
+                                                 int valid, int k) {
+  using G = Tile<FP8>;
   const int lane = fresh_lane();
-  if (k < 32 / NP) {
-    const int r = bw + NP * k;  // wave-uniform
-    const int rs = r < valid ? r : valid - 1;
-    lds_dma16(tile_g, rs * G::kRowBytes + 16 * lane, lds_addr(st + G::lat_base(r)));
+  if constexpr (!FP8) {
+    if (k < 32 / NP) {
+      const int r = bw + NP * k;  // wave-uniform
+      const int rs = r < valid ? r : valid - 1;
+      lds_dma16(tile_g, rs * G::kRowBytes + 16 * lane, lds_addr(st + G::lat_base(r)));
+    } else {
+      const int c8 = bw + NP * (k - 32 / NP);
+      const int r = 8 * c8 + (lane >> 3);
+      const int rs = r < valid ? r : valid - 1;
+      const int c = (lane & 7) ^ G::xrope(r);
+      lds_dma16(tile_g, rs * G::kRowBytes + G::kLat + 16 * c, lds_addr(st + G::kLatBytes + 1024 * c8));
+    }
   } else {
-    const int c8 = bw + NP * (k - 32 / NP);
-    const int r = 8 * c8 + (lane >> 3);
-    const int rs = r < valid ? r : valid - 1;
-    const int c = (lane & 7) ^ G::xrope(r);
-    lds_dma16(tile_g, rs * G::kRowBytes + G::kLat + 16 * c, lds_addr(st + G::kLatBytes + 1024 * c8));
+    static_assert(NP == 4, "E4M3 tiles: four loading waves");
+    if (k < 4) {
+      const int pr = bw + 4 * k;
+      const int r = pr + 16 * (lane >> 5);
+      const int rs = r < valid ? r : valid - 1;
+      const int c = (lane & 31) ^ G::xlat(r);
+      lds_dma16(tile_g, rs * G::kRowBytes + 16 * c, lds_addr(st + pr * 1056));
+    } else if (bw < 2) {
+      const int r = 16 * bw + (lane >> 2);
+      const int rs = r < valid ? r : valid - 1;
+      const int c = (lane & 3) ^ G::xrope(r);
+      lds_dma16(tile_g, rs * G::kRowBytes + G::kLat + 16 * c, lds_addr(st + G::kLatBytes + 1024 * bw));
+    } else {
+      lds_dma16(scale_g, 16 * (lane & 7), lds_addr(st + G::kLatBytes + G::kRopeBytes));
+    }
   }
 }
-template <int NP>
-__device__ __forceinline__ void pair_issue_bf16(const char* tile_g, LDS_AS char* st, int bw, int valid) {
+template <int NP, bool FP8>
+__device__ __forceinline__ void pair_issue_tile(const char* tile_g, const float* scale_g, LDS_AS char* st, int bw,
+                                                int valid) {
 #pragma unroll
-  for (int k = 0; k < kPairLoads<NP>; ++k) pair_issue_piece<NP>(tile_g, st, bw, valid, k);
+  for (int k = 0; k < kPairLoads<NP, FP8>; ++k) pair_issue_piece<NP, FP8>(tile_g, scale_g, st, bw, valid, k);
 }
 
-template <int NP, int ROLE>
+template <int NP, int ROLE, bool FP8>
 __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* smem, const PairSegment& sg,
                                              int pair, int tid) {
-  using G = Tile<false>;  // layout of the bf16 stages the MFMAs read
-  using Lds = PairLds<NP>;
+  using G = Tile<FP8>;  // layout of the stages the MFMAs read
+  using Lds = PairLds<NP, FP8>;
   constexpr int kRows = 32 * NP;  // rows of a workgroup
   constexpr int kBase = 18 * ROLE;  // first 16-dim step of this wave's half of the dot
   // Output columns: role 0 owns the 32-column blocks [0, 8), role 1 [8, 16).
@@ -1127,7 +1158,6 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
                   lds_addr(qrs + 1024 * j));
       }
     }
-    if (tid < 8) ((volatile LDS_AS uint32_t*)(smem + Lds::kRestart))[tid] = 0u;  // no requests, no scores yet
     wait_vmcnt<0>();
     __syncthreads();
     const int ln = fresh_lane(), h = ln >> 5, n = ln & 31;
@@ -1135,12 +1165,16 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
 #pragma unroll
     for (int s = 0; s < 18; ++s) {
       const int kk = kBase + s;
-      const bf16x8 f = kk < 32 ? *(const LDS_AS bf16x8*)(qst + n * kRowPitch + 2 * (16 * kk + 8 * h))
-                               : *(const LDS_AS bf16x8*)(qrs + n * 128 + 2 * (16 * (kk - 32) + 8 * h));
+      const bf16x8 f = kk < 32 ? *(const LDS_AS bf16x8*)(qst + n * kRowPitch + 2 * qfrag_dim<FP8>(kk, h))
+                               : *(const LDS_AS bf16x8*)(qrs + n * 128 + 2 * qfrag_dim<FP8>(kk - 32, h));
       if (s < kQReg) qf[s] = f;
       else kept[s - kQReg] = f;
     }
     __syncthreads();  // every wave has its fragments before the stages refill
+    // no restart requests, no partial scores yet (cleared only now: the query
+    // staging may cover these words; the first step's barrier orders the
+    // clear before every read)
+    if (tid < 8) ((volatile LDS_AS uint32_t*)(smem + Lds::kRestart))[tid] = 0u;
     LDS_AS char* qkeep = smem + Lds::kQKeep + (pair + NP * ROLE) * (kQLds * 1024);
 #pragma unroll
     for (int j = 0; j < kQLds; ++j) *(LDS_AS bf16x8*)(qkeep + 1024 * j + 16 * ln) = kept[j];
@@ -1169,33 +1203,70 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
   const int qk_off = Lds::kQKeep + (pair + NP * ROLE) * (kQLds * 1024);
 
   // The scores of the tile in st: this wave's 18 dot steps, one MFMA chain,
-  // key operands read from LDS two steps ahead.
+  // key operands read from LDS a few steps ahead.  E4M3 tiles: one 16-byte
+  // read per two steps (16 codes), converted to bf16 where used; each wave
+  // converts only the half of the keys it scores.
   auto scores = [&](const LDS_AS char* st, floatx16& S) {
     const int ln = fresh_lane(), h = ln >> 5, n = ln & 31;
     const int rho = swap_bits23(n);  // tile row feeding A-operand slot n
-    const LDS_AS char* kb = st + G::lat_base(rho) + 16 * h;
-    const LDS_AS char* rb = st + G::kLatBytes + rho * 128;
-    const int swr = G::xrope(rho);
     const LDS_AS char* qk = smem + qk_off + 16 * ln;
-    auto kread = [&](int kk) -> bf16x8 {
-      return kk < 32 ? *(const LDS_AS bf16x8*)(kb + 32 * kk)
-                     : *(const LDS_AS bf16x8*)(rb + 16 * ((2 * (kk - 32) + h) ^ swr));
+    constexpr int kAhead = 2;  // kept fragments are read this many steps before use
+    bf16x8 qk_reg[kQLds];
+    auto q_of = [&](int s) -> bf16x8 {  // this wave's query fragment of step s
+      if (s + kAhead >= kQReg && s + kAhead < 18)
+        qk_reg[s + kAhead - kQReg] = *(const LDS_AS bf16x8*)(qk + 1024 * (s + kAhead - kQReg));
+      return s < kQReg ? qf[s < kQReg ? s : 0] : qk_reg[s < kQReg ? 0 : s - kQReg];
     };
-    constexpr int KR = 4;  // key fragments in flight
-    bf16x8 kring[KR], qk_reg[kQLds];
-#pragma unroll
-    for (int r = 0; r < KR; ++r) kring[r] = kread(kBase + r);
-#pragma unroll
-    for (int s = 0; s < 18; ++s) {
-      const bf16x8 a = kring[s % KR];
-      if (s + KR < 18) kring[s % KR] = kread(kBase + s + KR);
-      constexpr int kAhead = 2;  // kept fragments are read this many steps before use
-      if (s + kAhead >= kQReg && s + kAhead < 18) qk_reg[s + kAhead - kQReg] = *(const LDS_AS bf16x8*)(qk + 1024 * (s + kAhead - kQReg));
-      const bf16x8 q = s < kQReg ? qf[s < kQReg ? s : 0] : qk_reg[s < kQReg ? 0 : s - kQReg];
+    auto chain = [&](int s, const bf16x8& a, const bf16x8& q) {
       if (s == 0) mfma_v0(S, a, q);
       else if (s < 17) mfma_v(S, a, q);
       else mfma_v_last(S, a, q);
-      __builtin_amdgcn_sched_barrier(0);  // keep the operand rings as written
+    };
+    if constexpr (!FP8) {
+      const LDS_AS char* kb = st + G::lat_base(rho) + 16 * h;
+      const LDS_AS char* rb = st + G::kLatBytes + rho * 128;
+      const int swr = G::xrope(rho);
+      auto kread = [&](int kk) -> bf16x8 {
+        return kk < 32 ? *(const LDS_AS bf16x8*)(kb + 32 * kk)
+                       : *(const LDS_AS bf16x8*)(rb + 16 * ((2 * (kk - 32) + h) ^ swr));
+      };
+      constexpr int KR = 4;  // key fragments in flight
+      bf16x8 kring[KR];
+#pragma unroll
+      for (int r = 0; r < KR; ++r) kring[r] = kread(kBase + r);
+#pragma unroll
+      for (int s = 0; s < 18; ++s) {
+        const bf16x8 a = kring[s % KR];
+        if (s + KR < 18) kring[s % KR] = kread(kBase + s + KR);
+        chain(s, a, q_of(s));
+        __builtin_amdgcn_sched_barrier(0);  // keep the operand rings as written
+      }
+    } else {
+      // chunk c (16 codes of row rho): dims 32 c + 16 h .. + 15 for c < 16,
+      // rope dims 32 (c - 16) + 16 h .. + 15 after; steps 2c and 2c + 1 take
+      // its first and last eight (the query fragments hold the same dims)
+      const LDS_AS char* kb = st + G::lat_base(rho) + 16 * (h ^ G::xlat(rho));
+      const LDS_AS char* rb = st + G::kLatBytes + rho * G::kRope;
+      const int swr = G::xrope(rho);
+      auto kread = [&](int c) -> uintx4 {
+        return c < 16 ? *(const LDS_AS uintx4*)(kb + 32 * c)
+                      : *(const LDS_AS uintx4*)(rb + 16 * ((2 * (c - 16) + h) ^ swr));
+      };
+      constexpr int KR = 2;  // key chunks in flight (four steps)
+      constexpr int kC0 = 9 * ROLE;  // this wave's first chunk
+      uintx4 kring[KR];
+#pragma unroll
+      for (int r = 0; r < KR; ++r) kring[r] = kread(kC0 + r);
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        const uintx4 raw = kring[c % KR];
+        if (c + KR < 9) kring[c % KR] = kread(kC0 + c + KR);
+        const bf16x8 a0 = e4m3x8_to_bf16(raw[0], raw[1]);
+        const bf16x8 a1 = e4m3x8_to_bf16(raw[2], raw[3]);
+        chain(2 * c, a0, q_of(2 * c));
+        chain(2 * c + 1, a1, q_of(2 * c + 1));
+        __builtin_amdgcn_sched_barrier(0);  // keep the operand rings as written
+      }
     }
   };
   // This wave's half of the value product of the tile in sv with weights pw
@@ -1205,40 +1276,83 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
   // (r0 & 15 <= 11), so every read is one base register plus an immediate.
   // (hook(s) runs after value MFMA s: role 1 issues its tile loads there)
   auto values = [&](const LDS_AS char* sv, const bf16x8 (&pw)[2], auto&& hook) {
-    const int ln = fresh_lane(), lh = ln >> 5, lsl = ln & 15, ldh = (ln >> 4) & 1;
-    const LDS_AS char* vb =
-        sv + G::lat_base(8 * lh + (lsl >> 2)) + 16 * (2 * ldh + ((lsl & 3) >> 1)) + 8 * (lsl & 1);
-    auto vread = [&](int x) -> bf16x8 {  // x: token half x / kNB, column block x % kNB
-      const LDS_AS char* b0 = vb + 16 * 1088 * (x / kNB) + 64 * (kCol0 + x % kNB);
-      const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)b0);
-      const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(b0 + 16 * 273));
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
     constexpr int VR = 2;
-    bf16x8 vring[VR];
+    if constexpr (!FP8) {
+      const int ln = fresh_lane(), lh = ln >> 5, lsl = ln & 15, ldh = (ln >> 4) & 1;
+      const LDS_AS char* vb =
+          sv + G::lat_base(8 * lh + (lsl >> 2)) + 16 * (2 * ldh + ((lsl & 3) >> 1)) + 8 * (lsl & 1);
+      auto vread = [&](int x) -> bf16x8 {  // x: token half x / kNB, column block x % kNB
+        const LDS_AS char* b0 = vb + 16 * 1088 * (x / kNB) + 64 * (kCol0 + x % kNB);
+        const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)b0);
+        const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(b0 + 16 * 273));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 vring[VR];
 #pragma unroll
-    for (int r = 0; r < VR; ++r) vring[r] = vread(r);
+      for (int r = 0; r < VR; ++r) vring[r] = vread(r);
 #pragma unroll
-    for (int s = 0; s < 2 * kNB; ++s) {
-      const bf16x8 v = vring[s % VR];
-      if (s + VR < 2 * kNB) vring[s % VR] = vread(s + VR);
-      mfma_v(acc[s % kNB], v, pw[s / kNB]);
-      hook(s);
+      for (int s = 0; s < 2 * kNB; ++s) {
+        const bf16x8 v = vring[s % VR];
+        if (s + VR < 2 * kNB) vring[s % VR] = vread(s + VR);
+        mfma_v(acc[s % kNB], v, pw[s / kNB]);
+        hook(s);
+      }
+    } else {
+      // E4M3: rows r0 = 8 lh + (lsl >> 1) and r0 + 16 share a block, 512 B
+      // apart, with the same chunk swizzle; one 8-byte transposed read gives
+      // eight tokens' codes of one column, converted where used
+      const int ln = fresh_lane(), lsl = ln & 15, ldh = (ln >> 4) & 1;
+      const int r0 = 8 * (ln >> 5) + (lsl >> 1);
+      const LDS_AS char* vb = sv + G::lat_base(r0) + 16 * (ldh ^ G::xlat(r0)) + 8 * (lsl & 1);
+      auto vread = [&](int x) -> intx2 {  // x: token half x / kNB, column block x % kNB
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS intx2*)(vb + 512 * (x / kNB) + 32 * (kCol0 + x % kNB)));
+      };
+      intx2 vring[VR];
+#pragma unroll
+      for (int r = 0; r < VR; ++r) vring[r] = vread(r);
+#pragma unroll
+      for (int s = 0; s < 2 * kNB; ++s) {
+        const intx2 v = vring[s % VR];
+        if (s + VR < 2 * kNB) vring[s % VR] = vread(s + VR);
+        mfma_v(acc[s % kNB], e4m3x8_to_bf16((unsigned)v[0], (unsigned)v[1]), pw[s / kNB]);
+        hook(s);
+      }
     }
   };
   auto no_hook = [](int) {};
   // Role 0, phase B: softmax of tile i from this wave's partial scores S and
   // the partner's (from the slot); writes the bf16 weights to the slot.
-  auto softmax = [&](auto with_mask, floatx16& S, const floatx4 (&sb)[4], int i, bf16x8 (&pw)[2]) {
+  // E4M3 (ts: the tile's 32 token scales in LDS, 8 copies; any copy
+  // serves): the scores are code-domain dots times the token's scale, the
+  // value product takes the weights times the scale and the normaliser the
+  // weights alone.  The scales are read where used, eight at a time (registers
+  // are scarce here); a masked token's weight stays 0 whatever its scale
+  // (past the request's end it may hold anything).
+  auto softmax = [&](auto with_mask, floatx16& S, const floatx4 (&sb)[4], int i, bf16x8 (&pw)[2],
+                     const LDS_AS float* ts) {
     constexpr bool kMask = decltype(with_mask)::value;
     const int ln = fresh_lane();
     // token 16 (e >> 3) + 8 h + (e & 7) is visible iff 16 (e >> 3) + (e & 7)
     // < lim - (cb + 32 i) - 8 h: one bound, compared against immediates
     const int lim_h = lim - (cb + 32 * i) - 8 * (ln >> 5);
+    auto scale8 = [&](int r, float (&sc)[8]) {  // scales of tokens 16 r + 8 h + j
+      const floatx4 u0 = *(const LDS_AS floatx4*)(ts + 16 * r + 8 * (ln >> 5));
+      const floatx4 u1 = *(const LDS_AS floatx4*)(ts + 16 * r + 8 * (ln >> 5) + 4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sc[c] = u0[c];
+        sc[4 + c] = u1[c];
+      }
+    };
     float mx_a = neg_inf(), mx_b = neg_inf();
+    float sc[8];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       float v = S[e] + sb[e >> 2][e & 3];
+      if constexpr (FP8) {
+        if ((e & 7) == 0) scale8(e >> 3, sc);
+        v *= sc[e & 7];
+      }
       if constexpr (kMask) v = 16 * (e >> 3) + (e & 7) < lim_h ? v : neg_inf();
       S[e] = v;
       if (e & 1) mx_b = __builtin_fmaxf(mx_b, v);
@@ -1265,6 +1379,15 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
       lb = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pw[1][2 * d], pw[1][2 * d + 1]}, ones, lb, false);
     }
     l_run += la + lb;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if ((e & 7) == 0) scale8(e >> 3, sc);
+        float w = (float)pw[e >> 3][e & 7] * sc[e & 7];
+        if constexpr (kMask) w = 16 * (e >> 3) + (e & 7) < lim_h ? w : 0.0f;
+        pw[e >> 3][e & 7] = (__bf16)w;
+      }
+    }
     // slot: weights [0, 2048) (the partner's partial scores there were read above)
     LDS_AS char* xw = smem + xs_off + 16 * ln;
     *(LDS_AS bf16x8*)xw = pw[0];
@@ -1281,7 +1404,9 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
   // scalar one would be waited for at the next LDS wait): it lands with the
   // tile loads, which step i + 1 waits for anyway.
   auto entry_of = [&](int i) { return kv_page_entry(p.page_table, p.MP, p.P, b, cb + 32 * i); };
-  auto tile_at = [&](int i, int page) { return kv + kv_row_of_page(page, p.P, cb + 32 * i) * G::kRowBytes; };
+  auto row_at = [&](int i, int page) { return kv_row_of_page(page, p.P, cb + 32 * i); };
+  auto tile_at = [&](int i, int page) { return kv + row_at(i, page) * G::kRowBytes; };
+  auto scales_at = [&](int i, int page) { return FP8 ? p.kv_scales + row_at(i, page) : nullptr; };
   auto page_ahead = [&](int i) {  // entries of tiles past the last are never read
     return i < ntiles ? entry_of(i)[fresh_lane() >> 6] : 0;  // (lane >> 6 == 0: one vector load)
   };
@@ -1291,7 +1416,8 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
     l_run = 0.0f;
     int pg_next = 0;  // role 1: page of tile i + 1 (in flight during step i - 1)
     if (ROLE == 1 && 0 < ntiles) {
-      pair_issue_bf16<NP>(tile_at(0, uniform_load(entry_of(0))), smem, pair, L - cb);
+      const int pg0 = uniform_load(entry_of(0));
+      pair_issue_tile<NP, FP8>(tile_at(0, pg0), scales_at(0, pg0), smem, pair, L - cb);
       pg_next = page_ahead(1);
     }
     int so_cur = 0;  // stage offsets of tiles i and i - 1 (three stages, rotating)
@@ -1346,25 +1472,28 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
           if (__builtin_amdgcn_readfirstlane(mark) > i) break;
           __builtin_amdgcn_s_sleep(1);
         }
+        const LDS_AS float* ts = (const LDS_AS float*)(smem + so_cur + G::kLatBytes + G::kRopeBytes);
         const bool full = __builtin_amdgcn_ballot_w64(lim - (cb + 32 * i) < 32) == 0;
         if (__builtin_amdgcn_readfirstlane((int)full))
-          softmax(std::false_type{}, S, sb, i, pw);
+          softmax(std::false_type{}, S, sb, i, pw, ts);
         else
-          softmax(std::true_type{}, S, sb, i, pw);
+          softmax(std::true_type{}, S, sb, i, pw, ts);
         values(smem + so_cur, pw, no_hook);
       } else {
         // the loads of tile i + 1 go out between the value MFMAs of tile
         // i - 1: issuing them takes a while, and here no wave waits on it
         const bool load_next = i + 1 < ntiles;
-        const char* tg = tile_at(load_next ? i + 1 : 0, __builtin_amdgcn_readfirstlane(pg_next));
+        const int pgn = __builtin_amdgcn_readfirstlane(pg_next);
+        const char* tg = tile_at(load_next ? i + 1 : 0, pgn);
+        const float* sgl = scales_at(load_next ? i + 1 : 0, pgn);
         const int vnext = L - (cb + 32 * (i + 1));
         auto issue = [&](int k) {
-          if (load_next && k < kPairLoads<NP>) pair_issue_piece<NP>(tg, smem + so_next, pair, vnext, k);
+          if (load_next && k < kPairLoads<NP, FP8>) pair_issue_piece<NP, FP8>(tg, sgl, smem + so_next, pair, vnext, k);
         };
         if (i >= 1) values(smem + so_prev, pw, issue);
         else issue(0);
 #pragma unroll
-        for (int k = i >= 1 ? 16 : 1; k < kPairLoads<NP>; ++k) issue(k);
+        for (int k = i >= 1 ? 16 : 1; k < kPairLoads<NP, FP8>; ++k) issue(k);
         pg_next = page_ahead(i + 2);
         if (i == ntiles) break;
       }
@@ -1464,10 +1593,10 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
   }
 }
 
-template <int NP>
+template <int NP, bool FP8>
 __global__ void __launch_bounds__(128 * NP, 1)
 mla_split_pair(SplitParams p, int groups) {
-  using Lds = PairLds<NP>;
+  using Lds = PairLds<NP, FP8>;
   constexpr int kWaves = 2 * NP;
   constexpr int kRows = 32 * NP;
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
@@ -1649,13 +1778,13 @@ mla_split_pair(SplitParams p, int groups) {
     // the previous segment's waves are done with all of the LDS
     __syncthreads();
     if (role == 0)
-      pair_segment<NP, 0>(p, smem, sg, pair, tid);
+      pair_segment<NP, 0, FP8>(p, smem, sg, pair, tid);
     else
-      pair_segment<NP, 1>(p, smem, sg, pair, tid);
+      pair_segment<NP, 1, FP8>(p, smem, sg, pair, tid);
   }
 }
 
-template <int NP>
+template <int NP, bool FP8>
 hipError_t launch_pair(const SplitParams& p, hipStream_t stream) {
   constexpr int kRows = 32 * NP;
   const int M = p.T * p.H;
@@ -1665,16 +1794,16 @@ hipError_t launch_pair(const SplitParams& p, hipStream_t stream) {
   const int64_t blocks = p.NB > 0   ? (int64_t)p.NB
                          : p.Sp > 0 ? 8LL * ((p.S + 7) / 8) * p.B * groups  // cascade: chunk-major per XCD
                                     : 8LL * groups * ((units + 7) / 8);
-  const size_t lds = (size_t)PairLds<NP>::kBytes;
+  const size_t lds = (size_t)PairLds<NP, FP8>::kBytes;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
-    attr_err = hipFuncSetAttribute((const void*)mla_split_pair<NP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    attr_err = hipFuncSetAttribute((const void*)mla_split_pair<NP, FP8>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)lds);
   });
   if (attr_err != hipSuccess) return attr_err;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((mla_split_pair<NP>), dim3((unsigned)blocks), dim3(128 * NP), lds, stream, p,
+  hipLaunchKernelGGL((mla_split_pair<NP, FP8>), dim3((unsigned)blocks), dim3(128 * NP), lds, stream, p,
                      groups);
   return hipGetLastError();
 }
@@ -2775,21 +2904,29 @@ Kernel pick_kernel(const SplitParams& p) {
   return p.kv_dtype == kFP8 ? Kernel::kMfmaFp8 : Kernel::kMfmaBf16;
 }
 
-// bf16 KV: the wave-pair kernel with 128-row workgroups.  (Workgroups of
-// two pairs would fill the chip where a uniform plan has fewer units than
-// compute units, but one wave per SIMD runs them slower than half the chip
-// runs the four-pair ones.)  The environment variable MLA_MFMA_KERNEL=four
-// (read at each launch) selects the four-wave kernel instead.
-hipError_t launch_bf16_mfma(const SplitParams& p, hipStream_t stream) {
+// bf16 and E4M3 KV: the wave-pair kernel with 128-row workgroups.
+// (Workgroups of two pairs would fill the chip where a uniform plan has fewer
+// units than compute units, but one wave per SIMD runs them slower than half
+// the chip runs the four-pair ones.)  The environment variable
+// MLA_MFMA_KERNEL=four (read at each launch) selects the four-wave kernel
+// instead, for either KV format.
+bool four_wave_selected() {
   const char* sel = getenv("MLA_MFMA_KERNEL");
-  if (sel && sel[0] == 'f') return launch_mfma<false, 4, 4>(p, stream);
-  return launch_pair<4>(p, stream);
+  return sel && sel[0] == 'f';
+}
+hipError_t launch_bf16_mfma(const SplitParams& p, hipStream_t stream) {
+  if (four_wave_selected()) return launch_mfma<false, 4, 4>(p, stream);
+  return launch_pair<4, false>(p, stream);
+}
+hipError_t launch_fp8_mfma(const SplitParams& p, hipStream_t stream) {
+  if (four_wave_selected()) return launch_mfma<true, 4, 8>(p, stream);
+  return launch_pair<4, true>(p, stream);
 }
 
 hipError_t launch_split(const SplitParams& p, hipStream_t stream) {
   switch (pick_kernel(p)) {
     case Kernel::kMfmaBf16: return launch_bf16_mfma(p, stream);
-    case Kernel::kMfmaFp8: return launch_mfma<true, 4, 8>(p, stream);
+    case Kernel::kMfmaFp8: return launch_fp8_mfma(p, stream);
     default: break;
   }
   const int M = p.T * p.H;

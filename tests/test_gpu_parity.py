@@ -460,10 +460,14 @@ def test_balanced_bf16_partials_error_against_fp32_partials(mla):
     assert eu[0] <= TOL["bf16"][0] and eu[1] <= TOL["bf16"][1]
 
 
-def test_four_wave_kernel_on_bf16(mla, monkeypatch):
-    """MLA_MFMA_KERNEL=four runs bf16 KV on the four-wave kernel (the one E4M3
-    KV always takes): uniform and balanced plans agree with the oracle."""
+def test_four_wave_kernel(mla, monkeypatch):
+    """MLA_MFMA_KERNEL=four runs bf16 and E4M3 KV on the four-wave kernel
+    instead of the wave-pair one: uniform and balanced plans agree with the
+    oracle."""
     monkeypatch.setenv("MLA_MFMA_KERNEL", "four")
     check_against_oracle(mla, synth.make_inputs(DS_SMALL), 2, "four-wave S=2")
     w = BALANCED_CASES["mixed"]
     check_against_oracle(mla, synth.make_inputs(w), 0, "four-wave balanced")
+    w8 = small(4, batch=4, seq_lens=("fixed", (1, 64, 300, 1000)), decoys=4, index=24)
+    check_against_oracle(mla, synth.make_inputs(w8), 3, "four-wave fp8 S=3")
+    check_against_oracle(mla, synth.make_inputs(BALANCED_CASES["fp8"]), 0, "four-wave fp8 balanced")
