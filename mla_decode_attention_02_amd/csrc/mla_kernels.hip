@@ -1211,11 +1211,12 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
     const int rho = swap_bits23(n);  // tile row feeding A-operand slot n
     const LDS_AS char* qk = smem + qk_off + 16 * ln;
     constexpr int kAhead = 2;  // kept fragments are read this many steps before use
-    bf16x8 qk_reg[kQLds];
+    bf16x8 qk_ring[kAhead];  // kept fragments in flight
     auto q_of = [&](int s) -> bf16x8 {  // this wave's query fragment of step s
-      if (s + kAhead >= kQReg && s + kAhead < 18)
-        qk_reg[s + kAhead - kQReg] = *(const LDS_AS bf16x8*)(qk + 1024 * (s + kAhead - kQReg));
-      return s < kQReg ? qf[s < kQReg ? s : 0] : qk_reg[s < kQReg ? 0 : s - kQReg];
+      const bf16x8 q = s < kQReg ? qf[s < kQReg ? s : 0] : qk_ring[(s < kQReg ? 0 : s - kQReg) % kAhead];
+      const int t = s + kAhead;  // the kept fragment read now
+      if (t >= kQReg && t < 18) qk_ring[(t - kQReg) % kAhead] = *(const LDS_AS bf16x8*)(qk + 1024 * (t - kQReg));
+      return q;
     };
     auto chain = [&](int s, const bf16x8& a, const bf16x8& q) {
       if (s == 0) mfma_v0(S, a, q);
@@ -1432,16 +1433,20 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
       const int so_next = so_cur == 2 * Lds::kCStage ? 0 : so_cur + Lds::kCStage;
       // (initialised here so that it is not carried from step to step)
       bf16x8 pw[2] = {bf16x8{}, bf16x8{}};  // role 0: the weights of tile i; role 1: those of tile i - 1
-      if (ROLE == 1) {
-        if (i >= 1) {  // the weights of tile i - 1
+      // role 1: the weights of tile i - 1 from the slot, read after its scores
+      // (not held through them) and before its partial scores overwrite the
+      // slot (LDS serves one wave's accesses in order)
+      auto read_weights = [&]() {
+        if (ROLE == 1 && i >= 1) {
           const int ln = fresh_lane();
           pw[0] = *(const LDS_AS bf16x8*)(smem + xs_off + 16 * ln);
           pw[1] = *(const LDS_AS bf16x8*)(smem + xs_off + 1024 + 16 * ln);
         }
-      }
+      };
       floatx16 S = __builtin_nondeterministic_value(S);  // defined by the scores when used
       if (i < ntiles) {
         scores(smem + so_cur, S);
+        read_weights();
         if (ROLE == 1) {
           LDS_AS char* xw = smem + xs_off + 16 * fresh_lane();
 #pragma unroll
@@ -1450,6 +1455,8 @@ __device__ __forceinline__ void pair_segment(const SplitParams& p, LDS_AS char* 
           // (LDS carries one wave's accesses in order: the mark lands after the scores)
           *(volatile LDS_AS int*)(smem + Lds::kReady + 4 * pr_slot) = i + 1;
         }
+      } else {
+        read_weights();
       }
       if (__builtin_amdgcn_readfirstlane((int)(rq[0] | rq[1] | rq[2] | rq[3])) != 0) {
         restart = true;
