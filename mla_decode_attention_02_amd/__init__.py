@@ -331,6 +331,9 @@ def combine_balanced(problem, num_workgroups, tile_prefix, slot_o, slot_lse, out
             or slot_o.numel() < 2 * nw * BALANCED_ROWS * problem.d_latent
             or slot_lse.numel() < 2 * nw * BALANCED_ROWS):
         raise ValueError("tile_prefix or slot buffers too small")
+    rows = problem.batch * problem.q_len * problem.num_heads
+    if out.numel() < rows * problem.d_latent or (lse is not None and lse.numel() < rows):
+        raise ValueError("out or lse too small")
     _check(library().mla_combine_balanced(ctypes.byref(problem), int(num_workgroups),
                                           _ptr(tile_prefix), _ptr(slot_o), _ptr(slot_lse),
                                           _ptr(out), _ptr(lse), _stream()),
