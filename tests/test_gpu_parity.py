@@ -80,6 +80,16 @@ def test_fp8_small(mla, S):
     check_against_oracle(mla, synth.make_inputs(w), S, f"fp8 S={S}")
 
 
+@pytest.mark.parametrize("H,T,S", [(16, 3, 1), (20, 1, 0), (64, 4, 2), (200, 1, 0)])
+def test_fp8_causal_and_ragged_rows(mla, H, T, S):
+    """E4M3 KV with causal drafts (masked tokens inside partial tiles carry
+    their token scales) and with row counts that leave padding rows in a
+    128-row group, on the uniform and balanced plans."""
+    w = small(4, batch=3, heads=H, q_len=T, causal=T > 1, seq_lens=("fixed", (5, 97, 650)),
+              decoys=3, index=27)
+    check_against_oracle(mla, synth.make_inputs(w), S, f"fp8 H={H} T={T} S={S}")
+
+
 def test_shared_prefix_small(mla):
     w = small(2, batch=3, seq_lens=("fixed", (129, 300, 1000)), shared_prefix=128, num_splits=4,
               decoys=4, index=25)
